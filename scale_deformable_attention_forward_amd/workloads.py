@@ -1,0 +1,167 @@
+"""Seeded synthetic workloads for multi-scale deformable attention.
+
+This module only draws inputs: it holds none of the method's arithmetic, and
+both the HIP path's tests/benchmark and the CPU oracle's tests take their
+inputs from it.
+
+Recipe (numpy ``default_rng(seed)``, draws in this order):
+  1. value ~ N(0, 1), drawn as (B, L, N_h, C_h) and cast to float32; the BNLC
+     layout is the transpose of the same numbers; bfloat16 values are the
+     round-to-nearest-even bfloat16 of those float32 numbers.
+  2. sampling locations, drawn as (B, N_q, N_h, N_l, N_p, 2) in float64 and
+     cast to float32; B2QHLP is the transpose of the same numbers.
+     Distributions: "uniform" U[lo, hi]; "clustered": a per-(b, q) centre
+     U[0, 1]^2 plus i.i.d. N(0, 0.02) offsets per (h, l, p, coordinate), not
+     clipped.
+  3. attention-weight logits ~ N(0, 1), softmax over the N_l * N_p axis of
+     each (b, q, h) in float64, then cast to float32.
+  4. grad_output ~ N(0, 1) of shape (B, N_q, N_h * C_h), float32, drawn from
+     its own generator when a seed for it is given.
+
+The five named workloads are Deformable-DETR-shaped feature pyramids.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ENCODER_LEVELS = ((100, 167), (50, 84), (25, 42), (13, 21))      # L = 22223
+SQUARE_LEVELS = ((128, 128), (64, 64), (32, 32), (16, 16))       # L = 21760
+TINY_LEVELS = ((8, 8), (4, 4))                                   # L = 80
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    levels: tuple
+    N_q: int | None          # None: one query per value pixel (N_q = L)
+    N_h: int
+    C_h: int
+    N_p: int
+    seed: int
+    loc_dist: str = "uniform"
+    loc_range: tuple = (0.0, 1.0)
+    value_dtype: str = "fp32"
+    value_layout: str = "BLNC"
+    sampling_locations_layout: str = "BQHLP2"
+    align_corners: bool = False
+    padding_mode: str = "zeros"
+    grad_seed: int | None = None
+    passes: tuple = field(default=("forward",))
+
+    @property
+    def L(self) -> int:
+        return int(sum(h * w for h, w in self.levels))
+
+    @property
+    def num_queries(self) -> int:
+        return self.L if self.N_q is None else self.N_q
+
+    @property
+    def N_l(self) -> int:
+        return len(self.levels)
+
+
+WORKLOADS = {
+    1: Workload("tiny_fp32_fwd_bwd", B=1, levels=TINY_LEVELS, N_q=16, N_h=2, C_h=8, N_p=2, seed=1,
+                loc_dist="uniform", loc_range=(0.0, 1.0), grad_seed=101,
+                passes=("forward", "backward")),
+    2: Workload("encoder_fp32_fwd", B=2, levels=ENCODER_LEVELS, N_q=None, N_h=8, C_h=32, N_p=4,
+                seed=2, loc_dist="uniform", loc_range=(-0.05, 1.05)),
+    3: Workload("decoder_fp32_fwd", B=8, levels=ENCODER_LEVELS, N_q=300, N_h=8, C_h=32, N_p=4,
+                seed=3, loc_dist="clustered"),
+    4: Workload("square_bf16_bnlc_b2qhlp_align_border_fwd", B=4, levels=SQUARE_LEVELS, N_q=None,
+                N_h=8, C_h=32, N_p=4, seed=4, loc_dist="uniform", loc_range=(-0.05, 1.05),
+                value_dtype="bf16", value_layout="BNLC", sampling_locations_layout="B2QHLP",
+                align_corners=True, padding_mode="border"),
+    5: Workload("encoder_fp32_bwd", B=2, levels=ENCODER_LEVELS, N_q=None, N_h=8, C_h=32, N_p=4,
+                seed=2, loc_dist="uniform", loc_range=(-0.05, 1.05), grad_seed=5,
+                passes=("backward",)),
+}
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bfloat16, returned as uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def level_start_index(levels) -> tuple:
+    starts, acc = [], 0
+    for h, w in levels:
+        starts.append(acc)
+        acc += h * w
+    return tuple(starts)
+
+
+def make_inputs(B, levels, N_q, N_h, C_h, N_p, seed, loc_dist="uniform", loc_range=(0.0, 1.0),
+                value_dtype="fp32", value_layout="BLNC", sampling_locations_layout="BQHLP2",
+                grad_seed=None):
+    """Draw one problem. Returns a dict of numpy arrays plus the level tables.
+
+    ``value`` is float32 (the exact values of the bfloat16 numbers when
+    value_dtype == "bf16"); ``value_bf16_bits`` holds the uint16 patterns then.
+    """
+    levels = tuple((int(h), int(w)) for h, w in levels)
+    L = sum(h * w for h, w in levels)
+    N_l = len(levels)
+    rng = np.random.default_rng(seed)
+    value = rng.standard_normal((B, L, N_h, C_h)).astype(np.float32)
+    if loc_dist == "uniform":
+        lo, hi = loc_range
+        loc = rng.uniform(lo, hi, size=(B, N_q, N_h, N_l, N_p, 2))
+    elif loc_dist == "clustered":
+        centre = rng.uniform(0.0, 1.0, size=(B, N_q, 1, 1, 1, 2))
+        loc = centre + rng.normal(0.0, 0.02, size=(B, N_q, N_h, N_l, N_p, 2))
+    else:
+        raise ValueError(f"unknown location distribution {loc_dist!r}")
+    loc = loc.astype(np.float32)
+    logits = rng.standard_normal((B, N_q, N_h, N_l * N_p))
+    logits -= logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits)
+    attn = (e / e.sum(axis=-1, keepdims=True)).astype(np.float32).reshape(B, N_q, N_h, N_l, N_p)
+    out = {}
+    if value_dtype == "bf16":
+        bits = bf16_round_bits(value)
+        value = bf16_bits_to_f32(bits)
+        if value_layout == "BNLC":
+            bits = np.ascontiguousarray(bits.transpose(0, 2, 1, 3))
+        out["value_bf16_bits"] = bits
+    elif value_dtype != "fp32":
+        raise ValueError(f"unknown value dtype {value_dtype!r}")
+    if value_layout == "BNLC":
+        value = np.ascontiguousarray(value.transpose(0, 2, 1, 3))
+    if sampling_locations_layout == "B2QHLP":
+        loc = np.ascontiguousarray(loc.transpose(0, 5, 1, 2, 3, 4))
+    out.update(value=value, sampling_locations=loc, attention_weights=attn,
+               spatial_shapes=levels, level_start_index=level_start_index(levels),
+               value_dtype=value_dtype, value_layout=value_layout,
+               sampling_locations_layout=sampling_locations_layout)
+    if grad_seed is not None:
+        g = np.random.default_rng(grad_seed).standard_normal((B, N_q, N_h * C_h)).astype(np.float32)
+        if value_dtype == "bf16":
+            g = bf16_bits_to_f32(bf16_round_bits(g))
+        out["grad_output"] = g
+    return out
+
+
+def make_workload(wl: Workload | int, grad_seed=None):
+    """Inputs for a named workload (or its number), plus its mode flags."""
+    if isinstance(wl, int):
+        wl = WORKLOADS[wl]
+    g = wl.grad_seed if grad_seed is None else grad_seed
+    d = make_inputs(wl.B, wl.levels, wl.num_queries, wl.N_h, wl.C_h, wl.N_p, wl.seed,
+                    loc_dist=wl.loc_dist, loc_range=wl.loc_range, value_dtype=wl.value_dtype,
+                    value_layout=wl.value_layout,
+                    sampling_locations_layout=wl.sampling_locations_layout, grad_seed=g)
+    d.update(align_corners=wl.align_corners, padding_mode=wl.padding_mode)
+    return d
