@@ -1,0 +1,250 @@
+"""Benchmark of the multi-scale deformable attention hot path on one MI355X.
+
+One step = one forward (msda_forward) plus one backward (msda_backward, all
+three gradients) over the encoder-shaped workload: B=2, four levels
+(100,167),(50,84),(25,42),(13,21) so L = N_q = 22223, N_h=8, C_h=32, N_p=4,
+float32, BLNC / BQHLP2, zeros padding, align_corners off; locations
+U[-0.05, 1.05], softmax attention weights, grad_output ~ N(0, 1). Inputs are
+seeded, synthetic, and resident in HBM before the timed region starts.
+
+Prints ONE JSON line. `value` is queries/s of whole steps; `roofline` is the
+dominant kernel's algorithmic bytes per launch over its average launch time
+(HIP events on the stream the kernels run on) against the 8 TB/s HBM peak;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+METRIC = "queries/s and effective gathered HBM GB/s (% of peak), fwd+bwd, 1 MI355X"
+WORKLOAD_NUM = 5                # encoder shapes with grad_output (the forward uses the same arrays)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps with a 1 GiB scratch write between them (caches cold)")
+    return ap.parse_args()
+
+
+def inrange_corners(d):
+    """(sample, corner) pairs whose corner lies inside its level: the corners the
+    method must read. Float32 coordinate map as in the kernels."""
+    loc = d["sampling_locations"]
+    n = 0
+    for l, (H, W) in enumerate(d["spatial_shapes"]):
+        ux = loc[:, :, :, l, :, 0].astype(np.float64)
+        uy = loc[:, :, :, l, :, 1].astype(np.float64)
+        # loc*W - 0.5 is exact in float64 here; one rounding to float32 = fmaf
+        x = (ux * W - 0.5).astype(np.float32)
+        y = (uy * H - 0.5).astype(np.float32)
+        x0 = np.floor(x).astype(np.int64)
+        y0 = np.floor(y).astype(np.int64)
+        for dx in (0, 1):
+            okx = (x0 + dx >= 0) & (x0 + dx < W)
+            for dy in (0, 1):
+                n += int((okx & (y0 + dy >= 0) & (y0 + dy < H)).sum())
+    return n
+
+
+def byte_counts(d):
+    """Algorithmic bytes per launch: nominal (4 corners per sample) and counted
+    (in-range corners only), plus the streams each kernel reads/writes once."""
+    B, N_q, N_h, N_l, N_p = d["attention_weights"].shape
+    C_h = d["value"].shape[-1]
+    s_v = 4
+    samples = B * N_q * N_h * N_l * N_p
+    corner_bytes = C_h * s_v
+    inr = inrange_corners(d)
+    loc_b, attn_b = samples * 8, samples * 4
+    out_b = B * N_q * N_h * C_h * s_v
+    value_b = d["value"].size * s_v
+    fwd_streams = loc_b + attn_b + out_b
+    # backward: grad_output + loc + attn in, grad_loc + grad_attn out, grad_value cleared once
+    bwd_streams = out_b + loc_b + attn_b + loc_b + attn_b + value_b
+    return {
+        "samples": samples,
+        "inrange_corners": inr,
+        "inrange_fraction": inr / (4 * samples),
+        "forward": {"nominal": 4 * samples * corner_bytes + fwd_streams,
+                    "counted": inr * corner_bytes + fwd_streams},
+        # re-gather + scatter (read-modify-write counted once)
+        "backward": {"nominal": 2 * 4 * samples * corner_bytes + bwd_streams,
+                     "counted": 2 * inr * corner_bytes + bwd_streams},
+        "queries": B * N_q,
+    }
+
+
+def cpu_baseline(d, target_s):
+    """The CPU oracle (fp64, OpenMP) on the same inputs: whole forward+backward
+    steps, repeated until about target_s seconds have run."""
+    import oracle
+    args = (d["spatial_shapes"], d["level_start_index"])
+    B, N_q = d["attention_weights"].shape[:2]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(d["value"], *args, d["sampling_locations"], d["attention_weights"])
+        oracle.backward(d["grad_output"], d["value"], *args, d["sampling_locations"],
+                        d["attention_weights"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 50:
+            break
+    return {"value": reps * B * N_q / el, "unit": "queries/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full forward+backward step(s) of the same workload ({reps * B * N_q} "
+                      f"queries, {el:.1f} s), fp64 C oracle with OpenMP"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the kernels shard by head with no communication, see the design notes)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from scale_deformable_attention_forward_amd import binding
+    from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_workload
+
+    binding.load_library()   # raises if the HIP library is not built: no fallback
+    wl = WORKLOADS[WORKLOAD_NUM]
+    d = make_workload(WORKLOAD_NUM)
+    dev = torch.device("cuda:0")
+    v = torch.from_numpy(d["value"]).to(dev)
+    loc = torch.from_numpy(d["sampling_locations"]).to(dev)
+    attn = torch.from_numpy(d["attention_weights"]).to(dev)
+    gout = torch.from_numpy(d["grad_output"]).to(dev)
+    out = torch.empty(gout.shape, dtype=torch.float32, device=dev)
+    gv = torch.empty_like(v)
+    gl = torch.empty_like(loc)
+    ga = torch.empty_like(attn)
+    ss, ls = d["spatial_shapes"], d["level_start_index"]
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        binding.msda_forward(v, ss, ls, loc, attn, output=out, stream=stream)
+
+    def bwd():
+        binding.msda_backward(gout, v, ss, ls, loc, attn, grad_value=gv, grad_sampling_locations=gl,
+                              grad_attention_weights=ga, stream=stream)
+
+    for _ in range(a.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    K = a.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    b_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    span_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    ms_per_step = span_ms / K
+
+    cold = None
+    if a.cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        cf, cb = [], []
+        for i in range(min(K, 20)):
+            scratch.fill_(float(i))
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            fwd()
+            e[1].record(stream)
+            scratch.fill_(float(i) + 0.5)
+            e2 = torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+            bwd()
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            cf.append(e[0].elapsed_time(e[1]))
+            cb.append(e2.elapsed_time(e[2]))
+        cold = {"forward_ms_median": float(np.median(cf)), "backward_ms_median": float(np.median(cb))}
+        del scratch
+
+    bc = byte_counts(d)
+    Q = bc["queries"]
+
+    def kernel_line(name, ms):
+        avg_s = float(np.mean(ms)) * 1e-3
+        nominal = bc[name]["nominal"]
+        counted = bc[name]["counted"]
+        return {
+            "ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)),
+            "ms_p10": float(np.percentile(ms, 10)), "ms_p90": float(np.percentile(ms, 90)),
+            "queries_per_s": Q / avg_s,
+            "bytes_nominal": nominal, "bytes_counted": counted,
+            "gbs_nominal": nominal / avg_s / 1e9, "gbs_counted": counted / avg_s / 1e9,
+            "frac_counted": counted / avg_s / 1e9 / HBM_PEAK_GBS,
+        }
+
+    kf, kb = kernel_line("forward", f_ms), kernel_line("backward", b_ms)
+    dom_name, dom = ("backward", kb) if kb["ms_mean"] >= kf["ms_mean"] else ("forward", kf)
+    achieved = dom["bytes_nominal"] / (dom["ms_mean"] * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        "bytes_per_launch": dom["bytes_nominal"],
+        "note": "algorithmic bytes = nominal per-query figure x queries (4 corners per sample); "
+                "achieved_counted uses in-range corners only",
+        "achieved_counted": dom["gbs_counted"],
+    }
+    res = {
+        "metric": METRIC,
+        "value": Q / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Deformable-DETR-shaped pyramid, no dataset)",
+        "config": {"workload": f"{wl.name} forward+backward: B={wl.B}, levels={list(wl.levels)}, "
+                               f"L=N_q={wl.L}, N_h={wl.N_h}, C_h={wl.C_h}, N_l={wl.N_l}, N_p={wl.N_p}, "
+                               "BLNC/BQHLP2, zeros padding, align_corners=False",
+                   "global_batch": wl.B, "queries_per_step": Q, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {"forward": kf, "backward": kb},
+        "inrange_corner_fraction": bc["inrange_fraction"],
+        "wall_s_timed": wall,
+    }
+    if cold is not None:
+        res["cold_caches"] = cold
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * msda.h - C ABI of the gfx950 (MI355X) multi-scale deformable attention library.
+ *
+ * Two operations, each a call below:
+ *   msda_forward   - "MS Deformable Attention Kernel API Reference"
+ *                    (Background; Parameters; Returns).
+ *   msda_backward  - "MS Deformable Attention Backward Kernel API Reference"
+ *                    (Background; Parameters: grad_output and the
+ *                    compute_grad_* flags; Returns; Notes).
+ *
+ * Notation follows the pages: B batch, N_q queries, N_h heads, C_h channels
+ * per head, N_l pyramid levels, N_p sampling points per (query, head, level),
+ * L = sum over levels of H_l * W_l.
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays in the
+ *    stated layout. The caller owns every buffer; the library allocates
+ *    nothing and keeps no state between calls; calls are reentrant.
+ *  - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *    returns before it finishes. Outputs must not overlap inputs.
+ *  - Every check happens on the host before the first HIP call, so an error
+ *    status means nothing was enqueued. No call aborts or throws.
+ *  - value, output, grad_output and grad_value share problem->value_dtype;
+ *    sampling locations, attention weights and their gradients are float32;
+ *    all accumulation is float32.
+ *  - Pointers need the natural alignment of their element type.
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSDA_ABI_VERSION 1
+#define MSDA_MAX_LEVELS 16
+
+typedef enum msda_status {
+    MSDA_OK = 0,
+    MSDA_ERR_INVALID_ARGUMENT = 1,  /* NULL/misaligned/overlapping pointer, bad size or enum */
+    MSDA_ERR_INVALID_LEVELS = 2,    /* H or W < 1, L != sum H*W, starts not the prefix sums */
+    MSDA_ERR_NOTHING_TO_COMPUTE = 3,/* backward with all three gradient outputs NULL */
+    MSDA_ERR_UNSUPPORTED = 4,       /* N_l > MSDA_MAX_LEVELS, a size past the index range,
+                                       or a dtype the call does not implement */
+    MSDA_ERR_WORKSPACE_TOO_SMALL = 5,
+    MSDA_ERR_HIP = 6                /* a HIP launch reported an error */
+} msda_status;
+
+/* value layouts ("MS Deformable Attention Kernel API Reference", Parameters: value) */
+typedef enum msda_value_layout {
+    MSDA_VALUE_BLNC = 0,  /* (B, L, N_h, C_h) */
+    MSDA_VALUE_BNLC = 1   /* (B, N_h, L, C_h) */
+} msda_value_layout;
+
+/* sampling_locations layouts (same page, Parameters: sampling_locations);
+   the size-2 axis holds (x, y): x along W, y along H. */
+typedef enum msda_loc_layout {
+    MSDA_LOC_BQHLP2 = 0,  /* (B, N_q, N_h, N_l, N_p, 2) */
+    MSDA_LOC_B2QHLP = 1   /* (B, 2, N_q, N_h, N_l, N_p) */
+} msda_loc_layout;
+
+/* padding_mode (same page, Parameters; backward page, Notes) */
+typedef enum msda_padding {
+    MSDA_PAD_ZEROS = 0,   /* a corner outside the level reads 0 */
+    MSDA_PAD_BORDER = 1   /* the pixel coordinate is clamped into the level first */
+} msda_padding;
+
+typedef enum msda_dtype {
+    MSDA_F32 = 0,
+    MSDA_BF16 = 1         /* bfloat16 storage, float32 arithmetic, RNE stores */
+} msda_dtype;
+
+/*
+ * Problem description (host memory, read during the call only).
+ * spatial_shapes: N_l x 2 int64 (H_l, W_l) ("... Kernel API Reference",
+ *   Parameters: spatial_shapes). level_start_index: N_l int64, the start of
+ *   each level in the flattened L axis (Parameters: level_start_index); it
+ *   must be the exclusive prefix sum of H_l * W_l. Inside level l, pixel
+ *   (row i, column j) is element level_start_index[l] + i * W_l + j of L.
+ * align_corners != 0 maps a normalised coordinate u in [0, 1] to u * (W - 1);
+ *   0 maps it to u * W - 0.5, formed in float32 as fmaf(u, W, -0.5f)
+ *   (Parameters: align_corners; the page states the map for H, it is applied
+ *   to W the same way).
+ */
+typedef struct msda_problem {
+    int64_t B, L, N_q, N_h, C_h, N_l, N_p;
+    const int64_t* spatial_shapes;
+    const int64_t* level_start_index;
+    int32_t value_layout;               /* msda_value_layout */
+    int32_t sampling_locations_layout;  /* msda_loc_layout */
+    int32_t align_corners;              /* 0 or 1 */
+    int32_t padding_mode;               /* msda_padding */
+    int32_t value_dtype;                /* msda_dtype */
+} msda_problem;
+
+/*
+ * Forward sampler ("MS Deformable Attention Kernel API Reference",
+ * Background and Returns):
+ *   output[b, q, h*C_h + c] = sum_{l,p} attention_weights[b,q,h,l,p] * S_{l,p}[c]
+ * where S is the bilinear interpolation of level l of value[b, :, h, :] at
+ * sampling location [b,q,h,l,p] after the coordinate map and padding above.
+ *
+ *   value               (B, L, N_h, C_h) or (B, N_h, L, C_h), value_dtype
+ *   sampling_locations  (B, N_q, N_h, N_l, N_p, 2) or (B, 2, N_q, N_h, N_l, N_p), float32
+ *   attention_weights   (B, N_q, N_h, N_l, N_p), float32, used as given
+ *   output              (B, N_q, N_h * C_h), value_dtype, fully overwritten
+ *
+ * B == 0 or N_q == 0 is a valid empty problem (nothing is enqueued).
+ */
+msda_status msda_forward(const msda_problem* problem, const void* value,
+                         const float* sampling_locations, const float* attention_weights,
+                         void* output, hipStream_t stream);
+
+/*
+ * Bytes of device workspace msda_backward needs for `problem` (0 when none).
+ * The float32 path needs none.
+ */
+msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* bytes);
+
+/*
+ * Backward ("MS Deformable Attention Backward Kernel API Reference",
+ * Returns and Notes). With G = grad_output[b, q, h*C_h : (h+1)*C_h]:
+ *   grad_attention_weights[b,q,h,l,p] = <G, S_{l,p}>
+ *   grad_sampling_locations[..., x]   = A * <G, dS/dx> * dx/du_x   (same for y)
+ *   grad_value[b, corner, h, :]       = sum over every (q, l, p) whose in-range
+ *                                       corner it is of A * w_corner * G
+ * dx/du is W (align_corners off) or W - 1 (on), and 0 where border padding
+ * clamped the coordinate. The interpolant's derivative is that of the
+ * four-corner form (a right derivative at integer coordinates).
+ *
+ *   grad_output               (B, N_q, N_h * C_h), value_dtype
+ *   value, sampling_locations, attention_weights: as msda_forward
+ *   grad_value                same shape and layout as value, value_dtype, or NULL
+ *   grad_sampling_locations   same shape and layout as sampling_locations, float32, or NULL
+ *   grad_attention_weights    (B, N_q, N_h, N_l, N_p), float32, or NULL
+ *   workspace, workspace_bytes: at least msda_backward_workspace_size bytes
+ *                             (may be NULL/0 when that size is 0)
+ *
+ * A NULL gradient pointer skips that gradient (the compute_grad_* flags of the
+ * page); all three NULL returns MSDA_ERR_NOTHING_TO_COMPUTE ("at least one
+ * must be True"). Every non-NULL output is fully overwritten: grad_value is
+ * zeroed on the stream, then accumulated with float32 atomics, so its last
+ * bits may differ from run to run; the other two gradients are deterministic.
+ * value_dtype must be MSDA_F32 (MSDA_ERR_UNSUPPORTED otherwise).
+ */
+msda_status msda_backward(const msda_problem* problem, const void* grad_output, const void* value,
+                          const float* sampling_locations, const float* attention_weights,
+                          void* grad_value, float* grad_sampling_locations,
+                          float* grad_attention_weights, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* msda_status_string(msda_status status);
+
+/* MSDA_ABI_VERSION of the built library. */
+int msda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

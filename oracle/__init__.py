@@ -65,7 +65,14 @@ def bind(path):
     lib.oracle_backward.restype = i32
     lib.oracle_count_inrange_corners.argtypes = [i64] * 6 + [p64, p64] + [i32] * 4 + [pd]
     lib.oracle_count_inrange_corners.restype = i64
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
     return lib
+
+
+def max_threads() -> int:
+    """Threads the oracle's OpenMP loops use on this host."""
+    return int(_load().oracle_max_threads())
 
 
 def _f64(a):

@@ -48,6 +48,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <omp.h>
 
 enum { ORACLE_BLNC = 0, ORACLE_BNLC = 1 };
 enum { ORACLE_BQHLP2 = 0, ORACLE_B2QHLP = 1 };
@@ -286,3 +287,6 @@ int64_t oracle_count_inrange_corners(int64_t B, int64_t L, int64_t Nq, int64_t N
                     }
     return n;
 }
+
+/* Threads an OpenMP region of this library uses (for reporting only). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }

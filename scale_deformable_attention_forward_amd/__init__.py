@@ -1,0 +1,15 @@
+"""Multi-scale deformable attention on MI355X (gfx950): a C-ABI HIP library
+(``libmsda.so``, declared in ``include/msda.h``) and its thin Python binding.
+
+The binding (and with it torch and the library) is loaded on first use, so the
+seeded workload generators in ``workloads`` import without a GPU.
+"""
+__all__ = ["msda_forward", "msda_backward", "ms_deformable_attention", "MSDeformableAttention",
+           "load_library"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

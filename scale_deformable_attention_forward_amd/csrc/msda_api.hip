@@ -1,0 +1,260 @@
+// C ABI of the library: host-side validation and kernel dispatch.
+//
+// Every check below runs before the first HIP call, so a non-OK status means
+// nothing was enqueued. The entry points and their argument order follow the
+// signatures on "MS Deformable Attention Kernel API Reference" (API
+// Reference) and "MS Deformable Attention Backward Kernel API Reference"
+// (API Reference); the Trainium-only tuning knobs of the backward page
+// (gather/scatter indirection caps, replicated scatter buffers, dumps) have
+// no counterpart here.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/msda.h"
+#include "msda_device.h"
+
+namespace msda {
+hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
+                          const float* attn, void* out, hipStream_t stream);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_backward(const Geometry& g, int vec, int lpu, const float* grad_out, const float* value,
+                           const float* loc, const float* attn, float* grad_value, float* grad_loc,
+                           float* grad_attn, hipStream_t stream);
+}  // namespace msda
+
+namespace {
+
+using msda::Geometry;
+
+constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // kernels index with 32-bit offsets
+
+struct Sizes {
+    int64_t value_elems, loc_elems, attn_elems, out_elems;
+    size_t value_bytes, out_bytes;
+    int elem;  // bytes per value element
+};
+
+// Products that stay exact in int64 for any in-range problem or flag overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t* r)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+msda_status check_problem(const msda_problem* p, Geometry* g, Sizes* z)
+{
+    if (!p) return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->B < 0 || p->N_q < 0 || p->N_h < 1 || p->C_h < 1 || p->N_l < 1 || p->N_p < 1 || p->L < 1)
+        return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->value_layout != MSDA_VALUE_BLNC && p->value_layout != MSDA_VALUE_BNLC) return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->sampling_locations_layout != MSDA_LOC_BQHLP2 && p->sampling_locations_layout != MSDA_LOC_B2QHLP)
+        return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->align_corners != 0 && p->align_corners != 1) return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->padding_mode != MSDA_PAD_ZEROS && p->padding_mode != MSDA_PAD_BORDER) return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->value_dtype != MSDA_F32 && p->value_dtype != MSDA_BF16) return MSDA_ERR_INVALID_ARGUMENT;
+    if (p->N_l > MSDA_MAX_LEVELS) return MSDA_ERR_UNSUPPORTED;
+    if (!p->spatial_shapes || !p->level_start_index) return MSDA_ERR_INVALID_ARGUMENT;
+
+    // level table: H, W >= 1, starts are the exclusive prefix sums, L = sum H*W
+    int64_t total = 0;
+    for (int64_t l = 0; l < p->N_l; ++l) {
+        const int64_t H = p->spatial_shapes[2 * l], W = p->spatial_shapes[2 * l + 1];
+        if (H < 1 || W < 1) return MSDA_ERR_INVALID_LEVELS;
+        if (p->level_start_index[l] != total) return MSDA_ERR_INVALID_LEVELS;
+        int64_t hw;
+        if (!mul_ok(H, W, &hw) || hw >= kIndexLimit || total + hw >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+        total += hw;
+        // the float32 coordinate map needs pixel coordinates well inside 2^24
+        if (H + 2 >= ((int64_t)1 << 24) || W + 2 >= ((int64_t)1 << 24)) return MSDA_ERR_UNSUPPORTED;
+    }
+    if (total != p->L) return MSDA_ERR_INVALID_LEVELS;
+
+    int64_t S, t;
+    if (!mul_ok(p->N_l, p->N_p, &S)) return MSDA_ERR_UNSUPPORTED;
+    z->elem = p->value_dtype == MSDA_BF16 ? 2 : 4;
+    if (!mul_ok(p->B, p->L, &t) || !mul_ok(t, p->N_h, &t) || !mul_ok(t, p->C_h, &z->value_elems))
+        return MSDA_ERR_UNSUPPORTED;
+    if (!mul_ok(p->B, p->N_q, &t) || !mul_ok(t, p->N_h, &t) || !mul_ok(t, S, &z->attn_elems))
+        return MSDA_ERR_UNSUPPORTED;
+    if (!mul_ok(z->attn_elems, 2, &z->loc_elems)) return MSDA_ERR_UNSUPPORTED;
+    if (!mul_ok(p->B, p->N_q, &t) || !mul_ok(t, p->N_h, &t) || !mul_ok(t, p->C_h, &z->out_elems))
+        return MSDA_ERR_UNSUPPORTED;
+    if (z->value_elems >= kIndexLimit || z->loc_elems >= kIndexLimit || z->out_elems >= kIndexLimit)
+        return MSDA_ERR_UNSUPPORTED;
+    z->value_bytes = (size_t)z->value_elems * z->elem;
+    z->out_bytes = (size_t)z->out_elems * z->elem;
+
+    g->B = (int32_t)p->B;
+    g->L = (int32_t)p->L;
+    g->Nq = (int32_t)p->N_q;
+    g->Nh = (int32_t)p->N_h;
+    g->Ch = (int32_t)p->C_h;
+    g->Nl = (int32_t)p->N_l;
+    g->Np = (int32_t)p->N_p;
+    g->S = (int32_t)S;
+    g->bnlc = p->value_layout == MSDA_VALUE_BNLC;
+    g->b2q = p->sampling_locations_layout == MSDA_LOC_B2QHLP;
+    g->align_corners = p->align_corners;
+    g->border = p->padding_mode == MSDA_PAD_BORDER;
+    g->loc_pair_aligned = 0;
+    for (int l = 0; l < msda::kMaxLevels; ++l) {
+        const bool in = l < p->N_l;
+        g->lv.H[l] = in ? (int32_t)p->spatial_shapes[2 * l] : 1;
+        g->lv.W[l] = in ? (int32_t)p->spatial_shapes[2 * l + 1] : 1;
+        g->lv.start[l] = in ? (int32_t)p->level_start_index[l] : 0;
+    }
+    return MSDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int ilog2(int v)
+{
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+// Widest per-lane vector (in elements) that the channel count and every
+// pointer stepping by it allow: 16-byte loads where possible.
+int pick_vec(int64_t C_h, int elem, std::initializer_list<const void*> ptrs)
+{
+    for (int vec = 16 / elem; vec > 1; vec /= 2) {
+        if (C_h % vec) continue;
+        bool ok = true;
+        for (const void* p : ptrs) ok = ok && (!p || aligned(p, (size_t)vec * elem));
+        if (ok) return vec;
+    }
+    return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status msda_forward(const msda_problem* problem, const void* value, const float* sampling_locations,
+                         const float* attention_weights, void* output, hipStream_t stream)
+{
+    Geometry g;
+    Sizes z;
+    const msda_status st = check_problem(problem, &g, &z);
+    if (st != MSDA_OK) return st;
+    if (z.out_elems == 0) return MSDA_OK;  // B == 0 or N_q == 0
+    if (!value || !sampling_locations || !attention_weights || !output) return MSDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(value, z.elem) || !aligned(output, z.elem) || !aligned(sampling_locations, 4) ||
+        !aligned(attention_weights, 4))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    if (overlap(output, z.out_bytes, value, z.value_bytes) || overlap(output, z.out_bytes, sampling_locations, loc_bytes) ||
+        overlap(output, z.out_bytes, attention_weights, attn_bytes))
+        return MSDA_ERR_INVALID_ARGUMENT;
+
+    const int vec = pick_vec(problem->C_h, z.elem, {value, output});
+    const int lanes = (int)std::min<int64_t>(64, (problem->C_h + vec - 1) / vec);
+    g.lpu_log2 = ilog2(lanes);
+    const int64_t per_chunk = ((int64_t)1 << g.lpu_log2) * vec;
+    g.chunks = (int32_t)((problem->C_h + per_chunk - 1) / per_chunk);
+    const int64_t units = (int64_t)g.B * g.Nh * g.Nq * g.chunks;
+    const int64_t upb = msda::kBlock >> g.lpu_log2;
+    if (units >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    g.units = (int32_t)units;
+    g.blocks = (int32_t)((units + upb - 1) / upb);
+    g.loc_pair_aligned = aligned(sampling_locations, 8);
+    const hipError_t e = msda::launch_forward(g, problem->value_dtype == MSDA_BF16, vec, value,
+                                              sampling_locations, attention_weights, output, stream);
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* bytes)
+{
+    if (!bytes) return MSDA_ERR_INVALID_ARGUMENT;
+    Geometry g;
+    Sizes z;
+    const msda_status st = check_problem(problem, &g, &z);
+    if (st != MSDA_OK) return st;
+    if (problem->value_dtype != MSDA_F32) return MSDA_ERR_UNSUPPORTED;
+    *bytes = 0;
+    return MSDA_OK;
+}
+
+msda_status msda_backward(const msda_problem* problem, const void* grad_output, const void* value,
+                          const float* sampling_locations, const float* attention_weights, void* grad_value,
+                          float* grad_sampling_locations, float* grad_attention_weights, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    Geometry g;
+    Sizes z;
+    const msda_status st = check_problem(problem, &g, &z);
+    if (st != MSDA_OK) return st;
+    if (!grad_value && !grad_sampling_locations && !grad_attention_weights) return MSDA_ERR_NOTHING_TO_COMPUTE;
+    if (problem->value_dtype != MSDA_F32) return MSDA_ERR_UNSUPPORTED;
+    const bool empty = z.out_elems == 0;
+    if (!empty && (!grad_output || !value || !sampling_locations || !attention_weights))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const void* ins[4] = {grad_output, value, sampling_locations, attention_weights};
+    for (const void* p : ins)
+        if (p && !aligned(p, 4)) return MSDA_ERR_INVALID_ARGUMENT;
+    const void* outs[3] = {grad_value, grad_sampling_locations, grad_attention_weights};
+    for (const void* p : outs)
+        if (p && !aligned(p, 4)) return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    const size_t in_bytes[4] = {z.out_bytes, z.value_bytes, loc_bytes, attn_bytes};
+    const size_t out_bytes[3] = {z.value_bytes, loc_bytes, attn_bytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return MSDA_ERR_INVALID_ARGUMENT;
+    }
+
+    hipError_t e = hipSuccess;
+    if (grad_value) e = msda::launch_zero(static_cast<float*>(grad_value), z.value_elems, stream);
+    if (e != hipSuccess) return MSDA_ERR_HIP;
+    if (empty) return MSDA_OK;
+
+    const int vec = 1;
+    const int lpu = 1 << ilog2((int)std::min<int64_t>(64, problem->C_h));
+    const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
+    const int64_t upb = msda::kBlock / lpu;
+    g.lpu_log2 = ilog2(lpu);
+    g.chunks = 1;
+    g.units = (int32_t)units;
+    g.blocks = (int32_t)((units + upb - 1) / upb);
+    g.loc_pair_aligned = aligned(sampling_locations, 8) && (!grad_sampling_locations || aligned(grad_sampling_locations, 8));
+    e = msda::launch_backward(g, vec, lpu, static_cast<const float*>(grad_output), static_cast<const float*>(value),
+                              sampling_locations, attention_weights, static_cast<float*>(grad_value),
+                              grad_sampling_locations, grad_attention_weights, stream);
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+const char* msda_status_string(msda_status status)
+{
+    switch (status) {
+    case MSDA_OK: return "MSDA_OK";
+    case MSDA_ERR_INVALID_ARGUMENT: return "MSDA_ERR_INVALID_ARGUMENT: bad pointer, alignment, overlap, size or enum";
+    case MSDA_ERR_INVALID_LEVELS:
+        return "MSDA_ERR_INVALID_LEVELS: spatial_shapes / level_start_index inconsistent with L";
+    case MSDA_ERR_NOTHING_TO_COMPUTE: return "MSDA_ERR_NOTHING_TO_COMPUTE: all gradient outputs are NULL";
+    case MSDA_ERR_UNSUPPORTED: return "MSDA_ERR_UNSUPPORTED: size, level count or dtype not supported";
+    case MSDA_ERR_WORKSPACE_TOO_SMALL: return "MSDA_ERR_WORKSPACE_TOO_SMALL";
+    case MSDA_ERR_HIP: return "MSDA_ERR_HIP: a kernel launch failed";
+    }
+    return "unknown msda_status";
+}
+
+int msda_abi_version(void) { return MSDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal to the gfx950 library: kernel parameter blocks and small device
+// helpers shared by the forward and backward kernels. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msda {
+
+constexpr int kMaxLevels = 16;
+constexpr int kBlock = 256;      // 4 wave64s per workgroup
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr size_t kLdsBudget = 64 * 1024;  // dynamic LDS per workgroup kept within 64 KiB
+
+// Level table of the flattened pyramid ("MS Deformable Attention Kernel API
+// Reference", Parameters: spatial_shapes, level_start_index).
+struct Levels {
+    int32_t H[kMaxLevels];
+    int32_t W[kMaxLevels];
+    int32_t start[kMaxLevels];
+};
+
+// Everything a kernel needs to address one problem. Sizes are validated on
+// the host (every element count below 2^31 except where noted).
+struct Geometry {
+    int32_t B, L, Nq, Nh, Ch, Nl, Np, S;  // S = Nl * Np samples per (b, q, h)
+    int32_t bnlc;          // value layout is (B, N_h, L, C_h)
+    int32_t b2q;           // sampling-location layout is (B, 2, N_q, N_h, N_l, N_p)
+    int32_t align_corners;
+    int32_t border;
+    int32_t loc_pair_aligned;  // BQHLP2 (x, y) pairs may be read/written as one float2
+    int32_t lpu_log2;      // lanes per unit = 1 << lpu_log2
+    int32_t chunks;        // channel chunks per (b, q, h)
+    int32_t units;         // B * N_h * N_q * chunks
+    int32_t blocks;        // grid size
+    Levels lv;
+};
+
+// Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).
+// Renumber them so that each XCD receives one contiguous range of logical
+// blocks: consecutive logical blocks share a (b, h) slab of value, so each
+// XCD's L2 holds the slab it is working on.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk)
+{
+    const int q = nblk / kNumXcd, r = nblk % kNumXcd;
+    const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+    return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Level row of the table by a (possibly divergent) index, with static
+// indexing only so the table stays in kernel-argument memory.
+__device__ __forceinline__ void level_of(const Levels& lv, int l, int& H, int& W, int& start)
+{
+    H = 1; W = 1; start = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k) {
+        if (k == l) { H = lv.H[k]; W = lv.W[k]; start = lv.start[k]; }
+    }
+}
+
+// Normalised -> pixel coordinate along an axis of `size` pixels, in float32:
+// align_corners maps [0,1] to [0, size-1], otherwise to [-0.5, size-0.5]
+// ("MS Deformable Attention Kernel API Reference", Parameters: align_corners).
+__device__ __forceinline__ float pixel_coord(float u, int size, int align)
+{
+    return align ? u * (float)(size - 1) : __builtin_fmaf(u, (float)size, -0.5f);
+}
+
+// bfloat16 helpers (storage only; arithmetic is float32).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Load VEC consecutive elements of storage type T as float32.
+template <typename T, int VEC> struct VecIO;
+
+template <int VEC> struct VecIO<float, VEC> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[VEC])
+    {
+        if constexpr (VEC == 4) {
+            const float4 t = *reinterpret_cast<const float4*>(p);
+            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+        } else if constexpr (VEC == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(p);
+            v[0] = t.x; v[1] = t.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) v[i] = p[i];
+        }
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&v)[VEC])
+    {
+        if constexpr (VEC == 4) {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (VEC == 2) {
+            *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) p[i] = v[i];
+        }
+    }
+};
+
+template <int VEC> struct VecIO<uint16_t, VEC> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[VEC])
+    {
+        if constexpr (VEC == 8) {
+            const uint4 t = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        } else if constexpr (VEC == 4) {
+            const uint2 t = *reinterpret_cast<const uint2*>(p);
+            v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+            v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+        } else if constexpr (VEC == 2) {
+            const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+            v[0] = __uint_as_float(t << 16); v[1] = __uint_as_float(t & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) v[i] = bf16_to_f32(p[i]);
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[VEC])
+    {
+        if constexpr (VEC % 2 == 0) {
+            uint32_t w[VEC / 2];
+#pragma unroll
+            for (int i = 0; i < VEC / 2; ++i)
+                w[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
+            if constexpr (VEC == 8) {
+                *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else if constexpr (VEC == 4) {
+                *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+            } else {
+                *reinterpret_cast<uint32_t*>(p) = w[0];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) p[i] = f32_to_bf16_rne(v[i]);
+        }
+    }
+};
+
+}  // namespace msda

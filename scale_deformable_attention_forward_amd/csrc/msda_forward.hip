@@ -1,0 +1,201 @@
+// Forward sampler of multi-scale deformable attention for gfx950.
+//
+// Computes, for every (b, q, h) ("MS Deformable Attention Kernel API
+// Reference", Background and Returns):
+//   out[b, q, h*C_h + c] = sum_{l,p} A[b,q,h,l,p] * bilinear(level l of value[b,:,h,:], loc[b,q,h,l,p])[c]
+//
+// Work decomposition (one "unit" = one (b, h, q, channel chunk)):
+//  - a unit is owned by a group of LPU = 2^lpu_log2 lanes of one wave64;
+//    each lane holds VEC consecutive channels, so one corner fetch of a unit
+//    is a single contiguous C_h-run of value (128 B for 32 float32 channels)
+//    and a wave instruction fetches 64/LPU corners;
+//  - units are numbered (b, h, q) with q fastest and a workgroup takes
+//    256/LPU consecutive units, so a workgroup works inside one (b, h) slab
+//    of value; workgroup ids are renumbered so that each XCD sweeps one
+//    contiguous range of slabs (its L2 then holds the slab it gathers from);
+//  - per chunk of up to SC samples, the workgroup first stages every sample
+//    of its units in LDS, one thread per (unit, sample): the coordinate map,
+//    padding, floor, the four bilinear weights premultiplied by the attention
+//    weight (0 for a corner outside the level) and the corner's pixel index;
+//  - then each lane walks the staged samples and issues only the corner
+//    loads whose weight is nonzero, accumulating in float32 registers.
+#include "msda_device.h"
+
+namespace msda {
+
+struct FwdRecordPix {
+    int32_t pix;   // flat pixel index (along L) of corner (x0, y0)
+    int32_t W;     // row length of the sample's level, in pixels
+};
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
+                                                         const T* __restrict__ value,
+                                                         const float* __restrict__ loc,
+                                                         const float* __restrict__ attn,
+                                                         T* __restrict__ out)
+{
+    extern __shared__ float4 smem[];
+    const int lpu_log2 = g.lpu_log2;
+    const int upb = kBlock >> lpu_log2;
+    const int row = sc_max + 1;  // padded LDS row (one row per unit) against bank conflicts
+    float4* s_w = smem;
+    FwdRecordPix* s_pix = reinterpret_cast<FwdRecordPix*>(smem + upb * row);
+
+    const int tid = threadIdx.x;
+    const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
+    const int S = g.S;
+    const int plane = g.Nq * g.Nh * S;  // distance between the x and y planes (B2QHLP)
+
+    // The unit this lane works on.
+    const int grp = tid >> lpu_log2;
+    const int lig = tid & ((1 << lpu_log2) - 1);
+    const int u = u0 + grp;
+    int b = 0, h = 0, q = 0, chunk = 0;
+    {
+        int t = u;
+        chunk = t % g.chunks; t /= g.chunks;
+        q = t % g.Nq; t /= g.Nq;
+        h = t % g.Nh; b = t / g.Nh;
+    }
+    const int c0 = ((chunk << lpu_log2) + lig) * VEC;
+    const bool active = (u < g.units) && (c0 < g.Ch);
+    if (u >= g.units) { b = 0; h = 0; q = 0; }  // tail lanes: keep every address in range
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    const T* slab = value + (g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch) + c0;
+
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+
+    for (int s0 = 0; s0 < S; s0 += sc_max) {
+        const int sc = min(sc_max, S - s0);
+        if (s0 > 0) __syncthreads();
+        // ---- stage: one thread per (unit, sample) of this chunk ----
+        for (int i = tid; i < upb * sc; i += kBlock) {
+            const int gi = i / sc;
+            const int s = i - gi * sc;
+            const int uu = u0 + gi;
+            float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+            FwdRecordPix rp = {0, 1};
+            if (uu < g.units) {
+                int t = uu / g.chunks;
+                const int qq = t % g.Nq; t /= g.Nq;
+                const int hh = t % g.Nh, bb = t / g.Nh;
+                const int si = s0 + s;
+                const int l = si / g.Np;
+                int H, W, start;
+                level_of(g.lv, l, H, W, start);
+                const int idx = ((bb * g.Nq + qq) * g.Nh + hh) * S + si;
+                float ux, uy;
+                if (g.b2q) {
+                    const int j = bb * 2 * plane + (qq * g.Nh + hh) * S + si;
+                    ux = loc[j];
+                    uy = loc[j + plane];
+                } else if (g.loc_pair_aligned) {
+                    const float2 xy = *reinterpret_cast<const float2*>(loc + 2 * idx);
+                    ux = xy.x; uy = xy.y;
+                } else {
+                    ux = loc[2 * idx];
+                    uy = loc[2 * idx + 1];
+                }
+                const float a = attn[idx];
+                float x = pixel_coord(ux, W, g.align_corners);
+                float y = pixel_coord(uy, H, g.align_corners);
+                if (g.border) {
+                    // clamp into the level before taking corners (NaN lands on 0)
+                    x = fminf(fmaxf(x, 0.f), (float)(W - 1));
+                    y = fminf(fmaxf(y, 0.f), (float)(H - 1));
+                } else {
+                    // anything past [-1, W] reads nothing; keeps the int conversion safe
+                    x = fminf(fmaxf(x, -2.f), (float)(W + 1));
+                    y = fminf(fmaxf(y, -2.f), (float)(H + 1));
+                }
+                const float x0f = floorf(x), y0f = floorf(y);
+                const float fx = x - x0f, fy = y - y0f;
+                const int x0 = (int)x0f, y0 = (int)y0f;
+                // corner column / row inside the level
+                const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
+                const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
+                const float gx = 1.f - fx, gy = 1.f - fy;
+                w.x = (ix0 && iy0) ? a * (gx * gy) : 0.f;
+                w.y = (ix1 && iy0) ? a * (fx * gy) : 0.f;
+                w.z = (ix0 && iy1) ? a * (gx * fy) : 0.f;
+                w.w = (ix1 && iy1) ? a * (fx * fy) : 0.f;
+                rp.pix = start + y0 * W + x0;
+                rp.W = W;
+            }
+            s_w[gi * row + s] = w;
+            s_pix[gi * row + s] = rp;
+        }
+        __syncthreads();
+        // ---- gather: VEC channels per lane, only corners with nonzero weight ----
+        if (active) {
+            const float4* rw = s_w + grp * row;
+            const FwdRecordPix* rpix = s_pix + grp * row;
+#pragma unroll 4
+            for (int s = 0; s < sc; ++s) {
+                const float4 w = rw[s];
+                const FwdRecordPix rp = rpix[s];
+                const T* p00 = slab + rp.pix * pstride;
+                float v[VEC];
+                if (w.x != 0.f) {
+                    VecIO<T, VEC>::load(p00, v);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.x, v[i], acc[i]);
+                }
+                if (w.y != 0.f) {
+                    VecIO<T, VEC>::load(p00 + pstride, v);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.y, v[i], acc[i]);
+                }
+                if (w.z != 0.f) {
+                    VecIO<T, VEC>::load(p00 + rp.W * pstride, v);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.z, v[i], acc[i]);
+                }
+                if (w.w != 0.f) {
+                    VecIO<T, VEC>::load(p00 + (rp.W + 1) * pstride, v);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.w, v[i], acc[i]);
+                }
+            }
+        }
+    }
+    if (active) VecIO<T, VEC>::store(out + ((b * g.Nq + q) * g.Nh + h) * g.Ch + c0, acc);
+}
+
+// Host launcher: grid/LDS sizing for one instantiation.
+template <typename T, int VEC>
+static hipError_t launch_forward_t(const Geometry& g, const void* value, const float* loc,
+                                   const float* attn, void* out, hipStream_t stream)
+{
+    const int upb = kBlock >> g.lpu_log2;
+    const size_t rec = sizeof(float4) + sizeof(FwdRecordPix);
+    int sc = g.S < 16 ? g.S : 16;
+    while (sc > 1 && (size_t)upb * (sc + 1) * rec > kLdsBudget) --sc;
+    const size_t lds = (size_t)upb * (sc + 1) * rec;
+    hipLaunchKernelGGL((forward_kernel<T, VEC>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                       static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
+                          const float* attn, void* out, hipStream_t stream)
+{
+    if (bf16) {
+        switch (vec) {
+        case 8: return launch_forward_t<uint16_t, 8>(g, value, loc, attn, out, stream);
+        case 4: return launch_forward_t<uint16_t, 4>(g, value, loc, attn, out, stream);
+        case 2: return launch_forward_t<uint16_t, 2>(g, value, loc, attn, out, stream);
+        default: return launch_forward_t<uint16_t, 1>(g, value, loc, attn, out, stream);
+        }
+    }
+    switch (vec) {
+    case 4: return launch_forward_t<float, 4>(g, value, loc, attn, out, stream);
+    case 2: return launch_forward_t<float, 2>(g, value, loc, attn, out, stream);
+    default: return launch_forward_t<float, 1>(g, value, loc, attn, out, stream);
+    }
+}
+
+}  // namespace msda

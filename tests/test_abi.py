@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad problems on the host before any HIP call
+(so these calls enqueue nothing and touch no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+torch = pytest.importorskip("torch")
+from scale_deformable_attention_forward_amd import binding  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from scale_deformable_attention_forward_amd.build import build_library
+        build_library()
+    return binding.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:msda_status|const char\*|int)\s+(msda_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(binding.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.msda_abi_version() == 1
+    for code, name in binding.STATUS_NAMES.items():
+        assert lib.msda_status_string(code).decode().startswith(name)
+    assert lib.msda_status_string(99) is not None
+
+
+LEVELS = ((4, 6), (2, 3))
+STARTS = (0, 24)
+
+
+def _prob(**kw):
+    args = dict(B=1, L=30, N_q=5, N_h=2, C_h=8, spatial_shapes=LEVELS, level_start_index=STARTS, N_p=2)
+    over = {k: kw.pop(k) for k in list(kw) if k in args}
+    args.update(over)
+    return binding.make_problem(**args, **kw)
+
+
+# Fake but well-aligned, non-overlapping device addresses: every call below must
+# fail validation before it could dereference them.
+P = {k: ctypes.c_void_p(0x10_0000_0000 + i * 0x1_0000_0000) for i, k in
+     enumerate(["value", "loc", "attn", "out", "gout", "gv", "gl", "ga"])}
+
+
+def _fwd(lib, prob, value=P["value"], loc=P["loc"], attn=P["attn"], out=P["out"]):
+    return lib.msda_forward(ctypes.byref(prob), value, loc, attn, out, None)
+
+
+def _bwd(lib, prob, gv=P["gv"], gl=P["gl"], ga=P["ga"], gout=P["gout"], value=P["value"]):
+    return lib.msda_backward(ctypes.byref(prob), gout, value, P["loc"], P["attn"], gv, gl, ga,
+                             None, 0, None)
+
+
+def test_null_problem(lib):
+    assert lib.msda_forward(None, P["value"], P["loc"], P["attn"], P["out"], None) == 1
+    assert lib.msda_backward(None, P["gout"], P["value"], P["loc"], P["attn"], P["gv"], P["gl"],
+                             P["ga"], None, 0, None) == 1
+    sz = ctypes.c_size_t(7)
+    assert lib.msda_backward_workspace_size(None, ctypes.byref(sz)) == 1
+
+
+@pytest.mark.parametrize("field,val,code", [
+    ("B", -1, 1), ("N_q", -1, 1), ("N_h", 0, 1), ("C_h", 0, 1), ("N_p", 0, 1), ("L", 0, 1),
+    ("value_layout", 2, 1), ("sampling_locations_layout", 5, 1), ("align_corners", 2, 1),
+    ("padding_mode", 3, 1), ("value_dtype", 9, 1)])
+def test_bad_fields(lib, field, val, code):
+    prob, keep = _prob()
+    setattr(prob, field, val)
+    assert _fwd(lib, prob) == code
+    assert _bwd(lib, prob) == code
+
+
+@pytest.mark.parametrize("shapes,starts,L", [
+    (((4, 6), (2, 3)), (0, 23), 30),      # start is not the prefix sum
+    (((4, 6), (2, 3)), (1, 25), 30),      # first start not 0
+    (((4, 6), (2, 3)), (0, 24), 31),      # L != sum H*W
+    (((4, 0), (2, 3)), (0, 0), 6),        # W < 1
+    (((-1, 6), (2, 3)), (0, -6), 0),      # H < 1 (and L)
+])
+def test_bad_level_tables(lib, shapes, starts, L):
+    prob, keep = _prob(spatial_shapes=shapes, level_start_index=starts, L=L)
+    code = _fwd(lib, prob)
+    assert code in (1, 2)
+    assert code == 2 or L <= 0
+
+
+def test_too_many_levels(lib):
+    shapes = tuple((1, 1) for _ in range(17))
+    prob, keep = _prob(spatial_shapes=shapes, level_start_index=tuple(range(17)), L=17)
+    assert _fwd(lib, prob) == 4
+
+
+def test_index_range_limit(lib):
+    prob, keep = _prob(B=1 << 20, N_q=1 << 20)
+    assert _fwd(lib, prob) == 4
+
+
+def test_null_and_misaligned_pointers(lib):
+    prob, keep = _prob()
+    assert _fwd(lib, prob, value=None) == 1
+    assert _fwd(lib, prob, out=None) == 1
+    assert _fwd(lib, prob, loc=ctypes.c_void_p(P["loc"].value + 2)) == 1
+    assert _fwd(lib, prob, out=ctypes.c_void_p(P["out"].value + 1)) == 1
+
+
+def test_overlapping_output(lib):
+    prob, keep = _prob()
+    assert _fwd(lib, prob, out=ctypes.c_void_p(P["value"].value + 64)) == 1
+    assert _bwd(lib, prob, gl=ctypes.c_void_p(P["value"].value + 128)) == 1
+    assert _bwd(lib, prob, ga=ctypes.c_void_p(P["gl"].value + 4)) == 1
+
+
+def test_nothing_to_compute(lib):
+    prob, keep = _prob()
+    assert _bwd(lib, prob, gv=None, gl=None, ga=None) == 3
+
+
+def test_backward_bf16_not_implemented(lib):
+    prob, keep = _prob(value_dtype=torch.bfloat16)
+    assert _bwd(lib, prob) == 4
+    sz = ctypes.c_size_t(0)
+    assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 4
+
+
+def test_workspace_size_fp32_is_zero(lib):
+    prob, keep = _prob()
+    sz = ctypes.c_size_t(123)
+    assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
+    assert sz.value == 0
+
+
+def test_empty_forward_is_noop(lib):
+    prob, keep = _prob(N_q=0)
+    assert _fwd(lib, prob, value=None, loc=None, attn=None, out=None) == 0
+    prob, keep = _prob(B=0)
+    assert _fwd(lib, prob, value=None, loc=None, attn=None, out=None) == 0
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    v = torch.zeros(1, 30, 2, 8)
+    loc = torch.zeros(1, 5, 2, 2, 2, 2)
+    a = torch.zeros(1, 5, 2, 2, 2)
+    with pytest.raises(ValueError):
+        binding.msda_forward(v, LEVELS, STARTS, loc, a)

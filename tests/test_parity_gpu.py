@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element, under the comparison rule in
+helpers.py. Covers the five named workloads at full size, the flag sweep,
+ragged and degenerate shapes, selective gradients and run-to-run stability.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+from helpers import RTOL, compare, oracle_backward, oracle_forward, to_device, to_numpy
+from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_inputs, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _mk(levels=((7, 9), (4, 5), (1, 1)), B=2, N_q=37, N_h=3, C_h=8, N_p=3, seed=0,
+        value_dtype="fp32", value_layout="BLNC", loc_layout="BQHLP2", align=False, pad="zeros",
+        loc_range=(-0.1, 1.1), grad_seed=1):
+    d = make_inputs(B, levels, N_q, N_h, C_h, N_p, seed, loc_range=loc_range, value_dtype=value_dtype,
+                    value_layout=value_layout, sampling_locations_layout=loc_layout,
+                    grad_seed=grad_seed)
+    d.update(align_corners=align, padding_mode=pad)
+    return d
+
+
+def _gpu_forward(d, dev):
+    from scale_deformable_attention_forward_amd import msda_forward
+    import torch
+    t = to_device(d, dev)
+    out = msda_forward(t["value"], d["spatial_shapes"], d["level_start_index"], t["sampling_locations"],
+                       t["attention_weights"], d["value_layout"], d["sampling_locations_layout"],
+                       d["align_corners"], d["padding_mode"])
+    torch.cuda.synchronize()
+    return to_numpy(out)
+
+
+def _gpu_backward(d, dev, flags=(True, True, True)):
+    from scale_deformable_attention_forward_amd import msda_backward
+    import torch
+    t = to_device(d, dev)
+    res = msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                        t["sampling_locations"], t["attention_weights"], d["value_layout"],
+                        d["sampling_locations_layout"], d["align_corners"], d["padding_mode"],
+                        compute_grad_value=flags[0], compute_grad_sampling_locations=flags[1],
+                        compute_grad_attention_weights=flags[2])
+    torch.cuda.synchronize()
+    return tuple(to_numpy(r) for r in res)
+
+
+def _check_forward(d, dev, tag):
+    _say(f"forward {tag}")
+    got = _gpu_forward(d, dev)
+    want = oracle_forward(d)
+    return compare(f"forward {tag}", got, want, RTOL[d["value_dtype"]])
+
+
+def _check_backward(d, dev, tag, flags=(True, True, True)):
+    _say(f"backward {tag} flags={flags}")
+    got = _gpu_backward(d, dev, flags)
+    want = oracle_backward(d, compute_grad_value=flags[0], compute_grad_sampling_locations=flags[1],
+                           compute_grad_attention_weights=flags[2])
+    names = ("grad_value", "grad_sampling_locations", "grad_attention_weights")
+    for n, f, g, w in zip(names, flags, got, want):
+        if not f:
+            assert g is None
+            continue
+        compare(f"{n} {tag}", g, w, RTOL[d["value_dtype"]])
+
+
+# ------------------------------------------------------- named workloads ---
+
+@pytest.mark.parametrize("num", [1, 2, 3, 4])
+def test_forward_named_workload_full_size(num, gpu_device):
+    wl = WORKLOADS[num]
+    d = make_workload(num)
+    _check_forward(d, gpu_device, f"workload {num} {wl.name}")
+
+
+@pytest.mark.parametrize("num", [1, 5])
+def test_backward_named_workload_full_size(num, gpu_device):
+    wl = WORKLOADS[num]
+    d = make_workload(num)
+    _check_backward(d, gpu_device, f"workload {num} {wl.name}")
+
+
+# ------------------------------------------------------------- flag sweep ---
+
+SWEEP = list(itertools.product(["BLNC", "BNLC"], ["BQHLP2", "B2QHLP"], [False, True], ["zeros", "border"]))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("mode", SWEEP, ids=lambda m: "-".join(map(str, m)))
+def test_forward_flag_sweep(mode, dtype, gpu_device):
+    vl, ll, align, pad = mode
+    d = _mk(seed=3, value_dtype=dtype, value_layout=vl, loc_layout=ll, align=align, pad=pad)
+    _check_forward(d, gpu_device, f"sweep {mode} {dtype}")
+
+
+@pytest.mark.parametrize("mode", SWEEP, ids=lambda m: "-".join(map(str, m)))
+def test_backward_flag_sweep(mode, gpu_device):
+    vl, ll, align, pad = mode
+    d = _mk(seed=4, value_layout=vl, loc_layout=ll, align=align, pad=pad)
+    _check_backward(d, gpu_device, f"sweep {mode}")
+
+
+# ---------------------------------------------------- shapes and edge cases ---
+
+@pytest.mark.parametrize("C_h", [1, 2, 3, 4, 5, 16, 32, 64, 100, 256, 300])
+def test_channel_counts(C_h, gpu_device):
+    d = _mk(seed=5, C_h=C_h, N_q=19, N_h=2)
+    _check_forward(d, gpu_device, f"C_h={C_h}")
+    _check_backward(d, gpu_device, f"C_h={C_h}")
+
+
+@pytest.mark.parametrize("C_h", [8, 24, 32, 300])
+def test_channel_counts_bf16_forward(C_h, gpu_device):
+    d = _mk(seed=6, C_h=C_h, N_q=21, N_h=2, value_dtype="bf16", value_layout="BNLC")
+    _check_forward(d, gpu_device, f"bf16 C_h={C_h}")
+
+
+def test_single_level_single_point_single_pixel(gpu_device):
+    d = _mk(seed=7, levels=((1, 1),), N_p=1, loc_range=(-1.0, 2.0))
+    _check_forward(d, gpu_device, "1x1 level")
+    _check_backward(d, gpu_device, "1x1 level")
+    d = _mk(seed=7, levels=((1, 1),), N_p=1, pad="border", align=True)
+    _check_forward(d, gpu_device, "1x1 level border align")
+    _check_backward(d, gpu_device, "1x1 level border align")
+
+
+def test_sixteen_levels_many_points(gpu_device):
+    levels = tuple((1 + (i % 5), 2 + (i * 3) % 7) for i in range(16))
+    d = _mk(seed=8, levels=levels, N_p=5, N_q=23)
+    _check_forward(d, gpu_device, "16 levels x 5 points (S = 80 > one staging chunk)")
+    _check_backward(d, gpu_device, "16 levels x 5 points")
+
+
+def test_far_out_of_range_locations(gpu_device):
+    for pad in ("zeros", "border"):
+        d = _mk(seed=9, loc_range=(-50.0, 50.0), pad=pad)
+        _check_forward(d, gpu_device, f"far out of range {pad}")
+        _check_backward(d, gpu_device, f"far out of range {pad}")
+
+
+def test_ragged_query_counts(gpu_device):
+    for N_q in (1, 2, 31, 33, 65, 257):
+        d = _mk(seed=10 + N_q, N_q=N_q, C_h=32, N_h=1, B=1)
+        _check_forward(d, gpu_device, f"N_q={N_q}")
+        _check_backward(d, gpu_device, f"N_q={N_q}")
+
+
+@pytest.mark.parametrize("flags", [f for f in itertools.product([True, False], repeat=3) if any(f)])
+def test_selective_gradients(flags, gpu_device):
+    d = _mk(seed=11)
+    _check_backward(d, gpu_device, "selective", flags)
+
+
+def test_nothing_to_compute_raises(gpu_device):
+    d = _mk(seed=12)
+    with pytest.raises(ValueError):
+        _gpu_backward(d, gpu_device, (False, False, False))
+
+
+def test_empty_problems(gpu_device):
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward, msda_forward
+    d = _mk(seed=13, N_q=0)
+    t = to_device(d, gpu_device)
+    out = msda_forward(t["value"], d["spatial_shapes"], d["level_start_index"], t["sampling_locations"],
+                       t["attention_weights"])
+    assert out.shape == (2, 0, 24)
+    gv_init = torch.full_like(t["value"], 7.0)
+    gv, gl, ga = msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                               t["sampling_locations"], t["attention_weights"], grad_value=gv_init)
+    torch.cuda.synchronize()
+    assert gv is gv_init and not gv.any().item()   # nothing sampled: grad_value is all zeros
+
+
+def test_unaligned_views_take_narrower_vectors(gpu_device):
+    """Inputs that start one element into their allocation cannot use 16-byte loads."""
+    import torch
+    from scale_deformable_attention_forward_amd import msda_forward
+    d = _mk(seed=14, C_h=8)
+    t = to_device(d, gpu_device)
+    v = t["value"]
+    buf = torch.empty(v.numel() + 1, dtype=v.dtype, device=gpu_device)
+    vv = buf[1:].view(v.shape)
+    vv.copy_(v)
+    lbuf = torch.empty(t["sampling_locations"].numel() + 1, dtype=torch.float32, device=gpu_device)
+    ll = lbuf[1:].view(t["sampling_locations"].shape)
+    ll.copy_(t["sampling_locations"])
+    out = msda_forward(vv, d["spatial_shapes"], d["level_start_index"], ll, t["attention_weights"])
+    torch.cuda.synchronize()
+    compare("unaligned", to_numpy(out), oracle_forward(d), RTOL["fp32"])
+
+
+def test_pixel_centres_are_exact_on_gpu(gpu_device):
+    """One-hot weights at pixel centres of power-of-two levels return value bit for bit."""
+    levels = ((16, 32), (8, 16), (4, 4))
+    d = _mk(seed=15, levels=levels, N_q=40, N_h=2, C_h=32, N_p=2, grad_seed=None)
+    B, N_q, N_h, N_l, N_p = d["attention_weights"].shape
+    rng = np.random.default_rng(0)
+    loc = np.zeros((B, N_q, N_h, N_l, N_p, 2), np.float32)
+    A = np.zeros((B, N_q, N_h, N_l, N_p), np.float32)
+    want = np.zeros((B, N_q, N_h, 32), np.float32)
+    starts = d["level_start_index"]
+    for b, q, h in itertools.product(range(B), range(N_q), range(N_h)):
+        l, p = rng.integers(N_l), rng.integers(N_p)
+        H, W = levels[l]
+        i, j = rng.integers(H), rng.integers(W)
+        loc[b, q, h] = rng.uniform(0, 1, size=(N_l, N_p, 2))
+        loc[b, q, h, l, p] = ((j + 0.5) / W, (i + 0.5) / H)
+        A[b, q, h, l, p] = 1.0
+        want[b, q, h] = d["value"][b, starts[l] + i * W + j, h]
+    d.update(sampling_locations=loc, attention_weights=A)
+    got = _gpu_forward(d, gpu_device)
+    np.testing.assert_array_equal(got.reshape(want.shape), want)
+
+
+def test_repeat_runs_are_stable(gpu_device):
+    d = _mk(seed=16, C_h=32, N_q=300, N_h=8)
+    f1, f2 = _gpu_forward(d, gpu_device), _gpu_forward(d, gpu_device)
+    np.testing.assert_array_equal(f1, f2)
+    b1, b2 = _gpu_backward(d, gpu_device), _gpu_backward(d, gpu_device)
+    np.testing.assert_array_equal(b1[1], b2[1])   # grad_sampling_locations: no atomics
+    np.testing.assert_array_equal(b1[2], b2[2])   # grad_attention_weights: no atomics
+    compare("grad_value run to run", b1[0], b2[0], RTOL["fp32"])
+
+
+def test_autograd_function_matches_oracle(gpu_device):
+    import torch
+    from scale_deformable_attention_forward_amd import ms_deformable_attention
+    d = _mk(seed=17)
+    t = to_device(d, gpu_device)
+    v = t["value"].clone().requires_grad_(True)
+    loc = t["sampling_locations"].clone().requires_grad_(True)
+    a = t["attention_weights"].clone().requires_grad_(True)
+    out = ms_deformable_attention(v, d["spatial_shapes"], d["level_start_index"], loc, a)
+    out.backward(t["grad_output"])
+    torch.cuda.synchronize()
+    compare("autograd out", to_numpy(out), oracle_forward(d), RTOL["fp32"])
+    gv, gl, ga = oracle_backward(d)
+    compare("autograd grad_value", to_numpy(v.grad), gv, RTOL["fp32"])
+    compare("autograd grad_loc", to_numpy(loc.grad), gl, RTOL["fp32"])
+    compare("autograd grad_attn", to_numpy(a.grad), ga, RTOL["fp32"])
