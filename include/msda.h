@@ -117,8 +117,12 @@ msda_status msda_forward(const msda_problem* problem, const void* value,
                          void* output, hipStream_t stream);
 
 /*
- * Bytes of device workspace msda_backward needs for `problem` (0 when none).
- * The float32 path needs none.
+ * Bytes of device workspace msda_backward needs for `problem` (0 when none):
+ * 16 bytes per sample (B * N_q * N_h * N_l * N_p) when C_h % 4 == 0 and
+ * C_h <= 64, which is the shape of the destination-tiled grad_value pass;
+ * 0 otherwise. The workspace carries per-sample anchor corners, fractions and
+ * attention weights between the two backward kernels; its contents are
+ * scratch.
  */
 msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* bytes);
 
@@ -138,15 +142,20 @@ msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* by
  *   grad_value                same shape and layout as value, value_dtype, or NULL
  *   grad_sampling_locations   same shape and layout as sampling_locations, float32, or NULL
  *   grad_attention_weights    (B, N_q, N_h, N_l, N_p), float32, or NULL
- *   workspace, workspace_bytes: at least msda_backward_workspace_size bytes
- *                             (may be NULL/0 when that size is 0)
+ *   workspace, workspace_bytes: device memory, 16-byte aligned, at least
+ *                             msda_backward_workspace_size bytes, not
+ *                             overlapping any tensor (may be NULL/0 when that
+ *                             size is 0 or grad_value is NULL); else
+ *                             MSDA_ERR_WORKSPACE_TOO_SMALL
  *
  * A NULL gradient pointer skips that gradient (the compute_grad_* flags of the
  * page); all three NULL returns MSDA_ERR_NOTHING_TO_COMPUTE ("at least one
- * must be True"). Every non-NULL output is fully overwritten: grad_value is
- * zeroed on the stream, then accumulated with float32 atomics, so its last
- * bits may differ from run to run; the other two gradients are deterministic.
- * value_dtype must be MSDA_F32 (MSDA_ERR_UNSUPPORTED otherwise).
+ * must be True"). Every non-NULL output is fully overwritten. grad_value is
+ * computed per destination pixel: levels whose samples are spread over
+ * several workgroups are finished with float32 atomic adds into a cleared
+ * buffer, so their last bits may differ from run to run; grad_A and grad_loc
+ * are deterministic. value_dtype must be MSDA_F32 (MSDA_ERR_UNSUPPORTED
+ * otherwise).
  */
 msda_status msda_backward(const msda_problem* problem, const void* grad_output, const void* value,
                           const float* sampling_locations, const float* attention_weights,

@@ -18,14 +18,21 @@ namespace msda {
 hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
                           const float* attn, void* out, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
-hipError_t launch_backward(const Geometry& g, int vec, int lpu, const float* grad_out, const float* value,
-                           const float* loc, const float* attn, float* grad_value, float* grad_loc,
-                           float* grad_attn, hipStream_t stream);
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, const float* grad_out,
+                                const float* value, const float* loc, const float* attn, float* grad_value,
+                                float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream);
+hipError_t launch_backward_generic(const Geometry& g, int lpu, const float* grad_out, const float* value,
+                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
+                                   float* grad_attn, hipStream_t stream);
+struct AnchorWs;
+struct BandWs;
+size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws);
 }  // namespace msda
 
 namespace {
 
 using msda::Geometry;
+using msda::TilePlan;
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // kernels index with 32-bit offsets
 
@@ -139,6 +146,75 @@ int pick_vec(int64_t C_h, int elem, std::initializer_list<const void*> ptrs)
     return 1;
 }
 
+// Lanes per destination pixel / per unit on the fast backward path: C_h / 4
+// rounded up to a power of two (4 channels per lane).
+int fast_lanes(int64_t C_h) { return 1 << ilog2((int)((C_h + 3) / 4)); }
+
+// The fast backward path needs C_h % 4 == 0, C_h <= 64 and 16-byte aligned
+// channel rows; the tile pass packs pixel coordinates in 16 bits.
+bool fast_backward_shape(const msda_problem& p)
+{
+    if (p.C_h % 4 != 0 || p.C_h > 64) return false;
+    for (int64_t l = 0; l < p.N_l; ++l)
+        if (p.spatial_shapes[2 * l] > 60000 || p.spatial_shapes[2 * l + 1] > 60000) return false;
+    return true;
+}
+
+// Cut every level into bands (destination tiles) of rows x cols pixels: at
+// most kTilePixelsPerGroup pixels per lane group of the tile workgroup, at
+// most kTileBins anchor bins, at most kMaxBandsPerLevel bands per level. A
+// band whose list is expected to hold more than two LDS passes of entries
+// (coarse levels, where many samples land on each pixel) is split into
+// chunks of its list, one workgroup each, finished with atomic adds.
+// Returns false if a level cannot be tiled that way.
+bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
+{
+    const int64_t pmax = (int64_t)(msda::kTileBlock / lpu) * msda::kTilePixelsPerGroup;
+    const int64_t nsamp = p.N_q * p.N_p;
+    int64_t jobs = 0, bands = 0, cap = 0;
+    tp->any_chunked = 0;
+    for (int64_t l = 0; l < msda::kMaxLevels; ++l) {
+        tp->job_begin[l] = (int32_t)jobs;
+        tp->band_begin[l] = (int32_t)bands;
+        if (l >= p.N_l) {
+            tp->rows[l] = tp->row_bands[l] = tp->cols[l] = tp->col_bands[l] = tp->chunks[l] = 1;
+            continue;
+        }
+        const int64_t H = p.spatial_shapes[2 * l], W = p.spatial_shapes[2 * l + 1];
+        const int64_t cols = std::min<int64_t>(W, std::min<int64_t>(pmax, msda::kTileBins / 2 - 1));
+        int64_t rows = std::max<int64_t>(1, std::min<int64_t>(H, pmax / cols));
+        while (rows > 1 && (rows + 1) * (cols + 1) > msda::kTileBins) --rows;
+        const int64_t rb = (H + rows - 1) / rows, cb = (W + cols - 1) / cols;
+        if (rb * cb > msda::kMaxBandsPerLevel) return false;
+        // list entries of one band if locations spread evenly
+        const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;
+        int64_t chunks = (expect + 2 * msda::kTileEntries - 1) / (2 * msda::kTileEntries);
+        chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, 1024));
+        tp->rows[l] = (int32_t)rows;
+        tp->row_bands[l] = (int32_t)rb;
+        tp->cols[l] = (int32_t)cols;
+        tp->col_bands[l] = (int32_t)cb;
+        tp->chunks[l] = (int32_t)chunks;
+        if (chunks > 1) tp->any_chunked = 1;
+        jobs += rb * cb * chunks;
+        bands += rb * cb;
+        cap += nsamp * (cb > 1 ? 4 : 2);  // a sample touches at most 2 row bands x 2 column bands
+    }
+    tp->job_begin[msda::kMaxLevels] = (int32_t)jobs;
+    tp->jobs = (int32_t)jobs;
+    tp->bands = (int32_t)bands;
+    tp->cap = cap;
+    return jobs < kIndexLimit && cap < kIndexLimit;
+}
+
+// Fast-path workspace bytes for `p` (0 if the tiled pass cannot take it).
+size_t fast_workspace_bytes(const msda_problem& p, const Geometry& g)
+{
+    TilePlan tp = {};
+    if (!plan_tiles(p, fast_lanes(p.C_h), &tp)) return 0;
+    return msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,7 +260,7 @@ msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* by
     const msda_status st = check_problem(problem, &g, &z);
     if (st != MSDA_OK) return st;
     if (problem->value_dtype != MSDA_F32) return MSDA_ERR_UNSUPPORTED;
-    *bytes = 0;
+    *bytes = fast_backward_shape(*problem) ? fast_workspace_bytes(*problem, g) : 0;
     return MSDA_OK;
 }
 
@@ -193,8 +269,6 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
                           float* grad_sampling_locations, float* grad_attention_weights, void* workspace,
                           size_t workspace_bytes, hipStream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     Geometry g;
     Sizes z;
     const msda_status st = check_problem(problem, &g, &z);
@@ -220,13 +294,22 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
             if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return MSDA_ERR_INVALID_ARGUMENT;
     }
 
-    hipError_t e = hipSuccess;
-    if (grad_value) e = msda::launch_zero(static_cast<float*>(grad_value), z.value_elems, stream);
-    if (e != hipSuccess) return MSDA_ERR_HIP;
-    if (empty) return MSDA_OK;
-
-    const int vec = 1;
-    const int lpu = 1 << ilog2((int)std::min<int64_t>(64, problem->C_h));
+    // Fast path: 4 channels per lane and the destination-tiled grad_value
+    // pass (needs the workspace); otherwise one channel per lane and atomics.
+    const int64_t C_h = problem->C_h;
+    TilePlan tp = {};
+    const bool fast = fast_backward_shape(*problem) && plan_tiles(*problem, fast_lanes(C_h), &tp) &&
+                      aligned(value, 16) && aligned(grad_output, 16) && (!grad_value || aligned(grad_value, 16));
+    if (fast && grad_value && !empty) {
+        const size_t need = msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr);
+        if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < 4; ++i)
+            if (overlap(workspace, need, ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
+        for (int o = 0; o < 3; ++o)
+            if (overlap(workspace, need, outs[o], out_bytes[o])) return MSDA_ERR_INVALID_ARGUMENT;
+    }
+    const int lpu = fast ? fast_lanes(C_h) : 1 << ilog2((int)std::min<int64_t>(64, C_h));
     const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
     const int64_t upb = msda::kBlock / lpu;
     g.lpu_log2 = ilog2(lpu);
@@ -234,9 +317,25 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
     g.units = (int32_t)units;
     g.blocks = (int32_t)((units + upb - 1) / upb);
     g.loc_pair_aligned = aligned(sampling_locations, 8) && (!grad_sampling_locations || aligned(grad_sampling_locations, 8));
-    e = msda::launch_backward(g, vec, lpu, static_cast<const float*>(grad_output), static_cast<const float*>(value),
-                              sampling_locations, attention_weights, static_cast<float*>(grad_value),
-                              grad_sampling_locations, grad_attention_weights, stream);
+    if (fast && grad_value && !empty && (int64_t)tp.jobs * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+
+    hipError_t e = hipSuccess;
+    // grad_value is cleared unless the tile pass stores every element itself
+    const bool clear = grad_value && (empty || !fast || tp.any_chunked);
+    if (clear) e = msda::launch_zero(static_cast<float*>(grad_value), z.value_elems, stream);
+    if (e != hipSuccess) return MSDA_ERR_HIP;
+    if (empty) return MSDA_OK;
+    if (fast) {
+        e = msda::launch_backward_fast(g, tp, lpu, static_cast<const float*>(grad_output),
+                                       static_cast<const float*>(value), sampling_locations, attention_weights,
+                                       static_cast<float*>(grad_value), grad_sampling_locations,
+                                       grad_attention_weights, workspace, stream);
+    } else {
+        e = msda::launch_backward_generic(g, lpu, static_cast<const float*>(grad_output),
+                                          static_cast<const float*>(value), sampling_locations, attention_weights,
+                                          static_cast<float*>(grad_value), grad_sampling_locations,
+                                          grad_attention_weights, stream);
+    }
     return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
 }
 

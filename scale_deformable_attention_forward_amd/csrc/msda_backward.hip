@@ -7,19 +7,30 @@
 //   grad_loc[b,q,h,l,p,x]  = A * <G, dS/dx> * dx/du_x    (same for y)
 //   grad_value[corner]    += A * w_corner * G             (every in-range corner)
 //
-// Decomposition: one unit = one (b, h, q), owned by LPU lanes of a wave64
-// with VEC consecutive channels per lane (more channels loop in chunks of
-// LPU*VEC). Units are numbered (b, h, q) with q fastest; workgroups are
-// renumbered per XCD as in the forward, so each XCD's L2 serves one (b, h)
-// slab for both the re-gather and the grad_value atomics.
-// Per chunk of up to SC samples the workgroup stages, one thread per
-// (unit, sample): the corner pixel index, the in-range mask, the fractional
-// offsets and the two coordinate slopes (0 where border padding clamped).
-// The lanes then re-gather the four corners, form S, dS/dx and dS/dy per
-// channel, reduce the three dot products over the unit's lanes with
-// cross-lane shuffles, and add A * w * G into grad_value with float32
-// atomics (global_atomic_add_f32, no return). grad_A and grad_loc go through
-// LDS and leave the workgroup as coalesced stores.
+// Fast path (C_h % 4 == 0, C_h <= 64, 16-byte aligned tensors), two kernels:
+//  1. backward_fast_kernel, one unit = one (b, h, q) owned by C_h/4 lanes with
+//     4 channels per lane. Per chunk of up to SC samples the workgroup stages,
+//     one thread per (unit, sample), the corner pixel index, in-range mask,
+//     fractional offsets, coordinate slopes (0 where border padding clamped)
+//     and the attention weight in LDS. The unit's lanes re-gather the four
+//     corners, form S, dS/dx and dS/dy, reduce the three dot products with
+//     DPP, and grad_A / grad_loc leave through LDS as coalesced stores. When
+//     grad_value is wanted, the staging also writes each sample's anchor
+//     corner (x0, y0) and fractions to the workspace.
+//  2. tile_scatter_kernel computes grad_value by destination instead of by
+//     source, so no float atomics sit on the hot path (global float atomics
+//     run at about one 128-byte line per request and LDS float atomics are an
+//     order of magnitude slower than LDS integer atomics on this part). Each
+//     level is cut into tiles of rows x cols pixels; a workgroup takes one
+//     tile (and, for dense coarse levels, one chunk of the level's samples),
+//     selects the samples whose 2x2 corner block touches the tile, bins them
+//     by anchor corner with LDS integer atomics, and then each destination
+//     pixel's lane group sums A * w * G over the four neighbouring anchor bins
+//     in registers (float64 within a pass). A tile written by one workgroup is stored; tiles split
+//     over several sample chunks are added with float atomics into a cleared
+//     grad_value (few: one per element per chunk).
+// Generic path (any C_h / alignment): backward_generic_kernel, one channel per
+// lane, grad_value through float atomics issued one channel per lane.
 #include <algorithm>
 
 #include "msda_device.h"
@@ -34,9 +45,9 @@ struct BwdRecord {
     int32_t mask;   // bit k: corner k = 2*dy + dx lies inside the level
     float a;        // attention weight
 };
+static_assert(sizeof(BwdRecord) == 2 * sizeof(float4), "records must tile two float4 slots");
 
-// grad_value is overwritten: cleared by a plain store kernel (a memset node
-// would misbehave inside a captured graph).
+// grad_value is overwritten: cleared by plain store kernels.
 __global__ __launch_bounds__(kBlock) void zero4_kernel(float4* __restrict__ p, int64_t n4)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -50,122 +61,644 @@ __global__ __launch_bounds__(kBlock) void zero1_kernel(float* __restrict__ p, in
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
 }
 
+// Sum over aligned groups of LPU lanes; every lane of a group gets the total
+// (pairwise butterfly, so all lanes add in the same order and agree bitwise).
 template <int LPU>
 __device__ __forceinline__ float group_sum(float v)
 {
-#pragma unroll
-    for (int m = LPU / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, LPU);
+    if constexpr (LPU >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));  // xor 1
+    if constexpr (LPU >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));  // xor 2
+    if constexpr (LPU >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)); // mirror 8
+    if constexpr (LPU >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)); // mirror 16
+    if constexpr (LPU >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (LPU >= 64) v += __shfl_xor(v, 32, 64);
     return v;
 }
 
-template <int VEC, int LPU>
-__global__ __launch_bounds__(kBlock) void backward_kernel(Geometry g, int sc_max,
-                                                          const float* __restrict__ grad_out,
-                                                          const float* __restrict__ value,
-                                                          const float* __restrict__ loc,
-                                                          const float* __restrict__ attn,
-                                                          float* __restrict__ grad_value,
-                                                          float* __restrict__ grad_loc,
-                                                          float* __restrict__ grad_attn)
+// Unit u -> (b, h, q) with q fastest.
+struct UnitIdx {
+    int b, h, q;
+};
+__device__ __forceinline__ UnitIdx unit_index(const Geometry& g, int u)
+{
+    UnitIdx r;
+    r.q = u % g.Nq;
+    const int t = u / g.Nq;
+    r.h = t % g.Nh;
+    r.b = t / g.Nh;
+    return r;
+}
+
+__device__ __forceinline__ int value_slab_offset(const Geometry& g, int b, int h)
+{
+    return g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch;
+}
+
+// Read the normalised (x, y) of sample si of unit (b, q, h).
+__device__ __forceinline__ void read_loc(const Geometry& g, const float* __restrict__ loc, int b, int q, int h,
+                                         int si, float& ux, float& uy)
+{
+    const int S = g.S;
+    if (g.b2q) {
+        const int plane = g.Nq * g.Nh * S;
+        const int j = b * 2 * plane + (q * g.Nh + h) * S + si;
+        ux = loc[j];
+        uy = loc[j + plane];
+    } else {
+        const int idx = ((b * g.Nq + q) * g.Nh + h) * S + si;
+        if (g.loc_pair_aligned) {
+            const float2 xy = *reinterpret_cast<const float2*>(loc + 2 * idx);
+            ux = xy.x;
+            uy = xy.y;
+        } else {
+            ux = loc[2 * idx];
+            uy = loc[2 * idx + 1];
+        }
+    }
+}
+
+// Coordinate map, padding and corners of one sample of level (H, W, start).
+// (x0, y0) receives the anchor corner in level pixels.
+__device__ __forceinline__ BwdRecord make_record(const Geometry& g, float ux, float uy, float a, int H, int W,
+                                                 int start, int& x0, int& y0)
+{
+    BwdRecord r;
+    float x = pixel_coord(ux, W, g.align_corners);
+    float y = pixel_coord(uy, H, g.align_corners);
+    float kx = g.align_corners ? (float)(W - 1) : (float)W;
+    float ky = g.align_corners ? (float)(H - 1) : (float)H;
+    if (g.border) {
+        if (!(x >= 0.f)) { x = 0.f; kx = 0.f; }  // also NaN
+        else if (x > (float)(W - 1)) { x = (float)(W - 1); kx = 0.f; }
+        if (!(y >= 0.f)) { y = 0.f; ky = 0.f; }
+        else if (y > (float)(H - 1)) { y = (float)(H - 1); ky = 0.f; }
+    } else {
+        // anything past [-1, W] reads nothing; keeps the int conversion safe
+        x = fminf(fmaxf(x, -2.f), (float)(W + 1));
+        y = fminf(fmaxf(y, -2.f), (float)(H + 1));
+    }
+    const float x0f = floorf(x), y0f = floorf(y);
+    x0 = (int)x0f;
+    y0 = (int)y0f;
+    const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
+    const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
+    r.fx = x - x0f;
+    r.fy = y - y0f;
+    r.kx = kx;
+    r.ky = ky;
+    r.pix = start + y0 * W + x0;
+    r.W = W;
+    r.mask = (ix0 && iy0 ? 1 : 0) | (ix1 && iy0 ? 2 : 0) | (ix0 && iy1 ? 4 : 0) | (ix1 && iy1 ? 8 : 0);
+    r.a = a;
+    return r;
+}
+
+// Per-sample anchors for the destination-tiled grad_value pass, laid out
+// [b * N_h + h][l][q][p]: anchor corner packed (x0 + 2) | (y0 + 2) << 16
+// (x0, y0 >= -2 after the clamp above), the two fractions and the attention
+// weight.
+struct AnchorWs {
+    uint32_t* anchor;
+    float* fx;
+    float* fy;
+    float* a;
+};
+
+// Stage one record per (unit, sample) of the chunk [s0, s0 + sc).
+__device__ __forceinline__ void stage_records(const Geometry& g, const float* __restrict__ loc,
+                                              const float* __restrict__ attn, BwdRecord* s_rec, int row,
+                                              int u0, int upb, int s0, int sc, AnchorWs ws)
+{
+    for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
+        const int gi = i / sc;
+        const int s = i - gi * sc;
+        const int uu = u0 + gi;
+        BwdRecord r = {0.f, 0.f, 0.f, 0.f, 0, 1, 0, 0.f};
+        if (uu < g.units) {
+            const UnitIdx ui = unit_index(g, uu);
+            const int si = s0 + s;
+            const int l = si / g.Np;
+            int H, W, start;
+            level_of(g.lv, l, H, W, start);
+            float ux, uy;
+            read_loc(g, loc, ui.b, ui.q, ui.h, si, ux, uy);
+            const float a = attn[((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si];
+            int x0, y0;
+            r = make_record(g, ux, uy, a, H, W, start, x0, y0);
+            if (ws.anchor) {
+                const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
+                ws.anchor[k] = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
+                ws.fx[k] = r.fx;
+                ws.fy[k] = r.fy;
+                ws.a[k] = a;
+            }
+        }
+        s_rec[gi * row + s] = r;
+    }
+}
+
+// Write grad_A and grad_loc of the chunk from LDS with coalesced stores.
+__device__ __forceinline__ void store_results(const Geometry& g, const float4* s_res, int row, int u0, int upb,
+                                              int s0, int sc, float* __restrict__ grad_loc,
+                                              float* __restrict__ grad_attn)
+{
+    for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
+        const int gi = i / sc;
+        const int s = i - gi * sc;
+        const int uu = u0 + gi;
+        if (uu >= g.units) continue;
+        const UnitIdx ui = unit_index(g, uu);
+        const int si = s0 + s;
+        const int idx = ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si;
+        const float4 res = s_res[gi * row + s];
+        if (grad_attn) grad_attn[idx] = res.x;
+        if (grad_loc) {
+            if (g.b2q) {
+                const int plane = g.Nq * g.Nh * g.S;
+                const int j = ui.b * 2 * plane + (ui.q * g.Nh + ui.h) * g.S + si;
+                grad_loc[j] = res.y;
+                grad_loc[j + plane] = res.z;
+            } else if (g.loc_pair_aligned) {
+                *reinterpret_cast<float2*>(grad_loc + 2 * idx) = make_float2(res.y, res.z);
+            } else {
+                grad_loc[2 * idx] = res.y;
+                grad_loc[2 * idx + 1] = res.z;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, float4-aligned
+// tensors. LPU lanes per unit, 4 channels per lane.
+template <int LPU>
+__global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max,
+                                                               const float* __restrict__ grad_out,
+                                                               const float* __restrict__ value,
+                                                               const float* __restrict__ loc,
+                                                               const float* __restrict__ attn,
+                                                               float* __restrict__ grad_loc,
+                                                               float* __restrict__ grad_attn, AnchorWs ws)
+{
+    constexpr int VEC = 4;
+    constexpr int upb = kBlock / LPU;  // units per workgroup
+
+    extern __shared__ float4 smem[];
+    const int row = sc_max + 1;
+    BwdRecord* s_rec = reinterpret_cast<BwdRecord*>(smem);
+    float4* s_res = smem + 2 * upb * row;
+
+    const int tid = threadIdx.x;
+    const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
+    const bool want_dots = grad_loc != nullptr || grad_attn != nullptr;
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+
+    const int grp = tid / LPU, lig = tid % LPU;
+    const int u = u0 + grp;
+    const bool unit_ok = u < g.units;
+    const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
+    const int c0 = lig * VEC;
+    const bool lane_ok = unit_ok && c0 < g.Ch;
+    const float* vslab = value + value_slab_offset(g, ui.b, ui.h) + c0;
+    float G[VEC] = {0.f, 0.f, 0.f, 0.f};
+    if (lane_ok && want_dots)
+        VecIO<float, VEC>::load(grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch + c0, G);
+
+    for (int s0 = 0; s0 < g.S; s0 += sc_max) {
+        const int sc = min(sc_max, g.S - s0);
+        if (s0 > 0) __syncthreads();
+        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, ws);
+        if (!want_dots) continue;
+        __syncthreads();
+        if (unit_ok) {
+            for (int s = 0; s < sc; ++s) {
+                const BwdRecord r = s_rec[grp * row + s];
+                const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
+                const float w00 = gxw * gyw, w01 = r.fx * gyw, w10 = gxw * r.fy, w11 = r.fx * r.fy;
+                const int o00 = r.pix * pstride;
+                const int o10 = o00 + r.W * pstride;
+                float v00[VEC] = {0.f, 0.f, 0.f, 0.f}, v01[VEC] = {0.f, 0.f, 0.f, 0.f};
+                float v10[VEC] = {0.f, 0.f, 0.f, 0.f}, v11[VEC] = {0.f, 0.f, 0.f, 0.f};
+                if (lane_ok) {
+                    if (r.mask & 1) VecIO<float, VEC>::load(vslab + o00, v00);
+                    if (r.mask & 2) VecIO<float, VEC>::load(vslab + o00 + pstride, v01);
+                    if (r.mask & 4) VecIO<float, VEC>::load(vslab + o10, v10);
+                    if (r.mask & 8) VecIO<float, VEC>::load(vslab + o10 + pstride, v11);
+                }
+                float pa = 0.f, px = 0.f, py = 0.f;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
+                    const float dx = gyw * (v01[i] - v00[i]) + r.fy * (v11[i] - v10[i]);
+                    const float dy = gxw * (v10[i] - v00[i]) + r.fx * (v11[i] - v01[i]);
+                    pa = __builtin_fmaf(G[i], smp, pa);
+                    px = __builtin_fmaf(G[i], dx, px);
+                    py = __builtin_fmaf(G[i], dy, py);
+                }
+                pa = group_sum<LPU>(pa);
+                px = group_sum<LPU>(px);
+                py = group_sum<LPU>(py);
+                if (lig == 0) s_res[grp * row + s] = make_float4(pa, r.a * px * r.kx, r.a * py * r.ky, 0.f);
+            }
+        }
+        __syncthreads();
+        store_results(g, s_res, row, u0, upb, s0, sc, grad_loc, grad_attn);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fast path, grad_value by destination.
+//
+// Workspace views: per-sample arrays written by backward_fast_kernel, the
+// per-(slab, band) counts / cursors / offsets and the band lists (SoA, `cap`
+// entries reserved per slab; entry = sample index k = q * N_p + p within its
+// (slab, level), anchor, fractions, attention weight).
+struct BandWs {
+    int* cnt;       // [slabs][bands]
+    int* cursor;    // [slabs][bands]
+    int* off;       // [slabs][bands + 1]
+    uint32_t* k;
+    uint32_t* anchor;
+    float* fx;
+    float* fy;
+    float* a;
+};
+
+struct LevelTiles {
+    int H, W, start, R, CW, nbr, nbc, nch, band0, job0;
+};
+
+// Tile geometry of level l (static indices only, so the plan stays in kernel-argument memory).
+__device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TilePlan& tp, int l)
+{
+    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k) {
+        if (k == l) {
+            t.H = g.lv.H[k];
+            t.W = g.lv.W[k];
+            t.start = g.lv.start[k];
+            t.R = tp.rows[k];
+            t.CW = tp.cols[k];
+            t.nbr = tp.row_bands[k];
+            t.nbc = tp.col_bands[k];
+            t.nch = tp.chunks[k];
+            t.band0 = tp.band_begin[k];
+            t.job0 = tp.job_begin[k];
+        }
+    }
+    return t;
+}
+
+// Level-local bands touched by the in-level corners of the 2x2 block anchored
+// at (x0, y0); returns how many (0..4).
+__device__ __forceinline__ int sample_bands(const LevelTiles& t, int x0, int y0, int (&out)[4])
+{
+    int rb[2], cb[2], nr = 0, nc = 0;
+    if (y0 >= 0 && y0 < t.H) rb[nr++] = y0 / t.R;
+    if (y0 + 1 >= 0 && y0 + 1 < t.H) {
+        const int r = (y0 + 1) / t.R;
+        if (nr == 0 || rb[0] != r) rb[nr++] = r;
+    }
+    if (x0 >= 0 && x0 < t.W) cb[nc++] = x0 / t.CW;
+    if (x0 + 1 >= 0 && x0 + 1 < t.W) {
+        const int c = (x0 + 1) / t.CW;
+        if (nc == 0 || cb[0] != c) cb[nc++] = c;
+    }
+    int n = 0;
+    for (int i = 0; i < nr; ++i)
+        for (int j = 0; j < nc; ++j) out[n++] = rb[i] * t.nbc + cb[j];
+    return n;
+}
+
+__device__ __forceinline__ void unpack_anchor(uint32_t a, int& x0, int& y0)
+{
+    x0 = (int)(a & 0xffffu) - 2;
+    y0 = (int)(a >> 16) - 2;
+}
+
+// Bucketing 1/3: per-(slab, band) sample counts. Grid (sample chunk, level, slab).
+__global__ __launch_bounds__(kBandBlock) void band_count_kernel(Geometry g, TilePlan tp,
+                                                                const uint32_t* __restrict__ anchor,
+                                                                int* __restrict__ cnt)
+{
+    __shared__ int hist[kMaxBandsPerLevel];
+    const int l = blockIdx.y, slab = blockIdx.z;
+    const LevelTiles t = level_tiles(g, tp, l);
+    const int nb = t.nbr * t.nbc;
+    const int nsamp = g.Nq * g.Np;
+    const int k0 = blockIdx.x * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
+    for (int i = threadIdx.x; i < nb; i += kBandBlock) hist[i] = 0;
+    __syncthreads();
+    const uint32_t* an = anchor + (size_t)(slab * g.Nl + l) * nsamp;
+    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
+        int x0, y0, bands[4];
+        unpack_anchor(an[k], x0, y0);
+        const int n = sample_bands(t, x0, y0, bands);
+        for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kBandBlock)
+        if (hist[i]) atomicAdd(&cnt[slab * tp.bands + t.band0 + i], hist[i]);
+}
+
+// Bucketing 2/3: exclusive prefix of the band counts of each slab.
+__global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const int* __restrict__ cnt,
+                                                           int* __restrict__ off)
+{
+    __shared__ int s_wave[kBlock / kWave];
+    const int slab = blockIdx.x, n = tp.bands;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int* c = cnt + slab * n;
+    int* o = off + slab * (n + 1);
+    int carry = 0;
+    for (int base = 0; base < n; base += kBlock) {
+        const int i = base + tid;
+        const int v = i < n ? c[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int u = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += u;
+        }
+        if (lane == kWave - 1) s_wave[wave] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int w = 0; w < kBlock / kWave; ++w) {
+            before += w < wave ? s_wave[w] : 0;
+            total += s_wave[w];
+        }
+        if (i < n) o[i] = carry + before + incl - v;
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) o[n] = carry;
+}
+
+// Bucketing 3/3: fill the band lists. Grid as band_count_kernel; each
+// workgroup reserves one contiguous run per band it touches.
+__global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
+                                                               const uint32_t* __restrict__ anchor,
+                                                               const float* __restrict__ sfx,
+                                                               const float* __restrict__ sfy,
+                                                               const float* __restrict__ sa)
+{
+    __shared__ int hist[kMaxBandsPerLevel];
+    __shared__ int base[kMaxBandsPerLevel];
+    const int l = blockIdx.y, slab = blockIdx.z;
+    const LevelTiles t = level_tiles(g, tp, l);
+    const int nb = t.nbr * t.nbc;
+    const int nsamp = g.Nq * g.Np;
+    const int k0 = blockIdx.x * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
+    for (int i = threadIdx.x; i < nb; i += kBandBlock) hist[i] = 0;
+    __syncthreads();
+    const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
+    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
+        int x0, y0, bands[4];
+        unpack_anchor(anchor[sbase + k], x0, y0);
+        const int n = sample_bands(t, x0, y0, bands);
+        for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kBandBlock) {
+        if (hist[i]) {
+            const int sb = slab * tp.bands + t.band0 + i;
+            base[i] = w.off[slab * (tp.bands + 1) + t.band0 + i] + atomicAdd(&w.cursor[sb], hist[i]);
+            hist[i] = 0;
+        }
+    }
+    __syncthreads();
+    const size_t lbase = (size_t)slab * tp.cap;
+    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
+        const uint32_t an = anchor[sbase + k];
+        int x0, y0, bands[4];
+        unpack_anchor(an, x0, y0);
+        const int n = sample_bands(t, x0, y0, bands);
+        if (n == 0) continue;
+        const float fx = sfx[sbase + k], fy = sfy[sbase + k], a = sa[sbase + k];
+        for (int j = 0; j < n; ++j) {
+            const size_t pos = lbase + base[bands[j]] + atomicAdd(&hist[bands[j]], 1);
+            w.k[pos] = (uint32_t)k;
+            w.anchor[pos] = an;
+            w.fx[pos] = fx;
+            w.fy[pos] = fy;
+            w.a[pos] = a;
+        }
+    }
+}
+
+// Tile kernel. LPU lanes per destination pixel (4 channels per lane),
+// kTileBlock / LPU pixel groups per workgroup, each owning up to
+// kTilePixelsPerGroup pixels of the tile.
+template <int LPU>
+__global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(Geometry g, TilePlan tp, BandWs w,
+                                                                  const float* __restrict__ grad_out,
+                                                                  float* __restrict__ grad_value)
+{
+    constexpr int NG = kTileBlock / LPU;
+    constexpr int PPG = kTilePixelsPerGroup;
+    constexpr int E = kTileEntries;
+    constexpr int kWaves = kTileBlock / kWave;
+    __shared__ float4 s_ent[E];              // (fx, fy, A, q)
+    __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
+    __shared__ uint16_t s_sorted[E];         // staged entries ordered by bin
+    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_sorted
+    __shared__ int s_cursor[kTileBins];
+    __shared__ int s_wave[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int slab = lb / tp.jobs;
+    const int job = lb - slab * tp.jobs;
+    const int b = slab / g.Nh, h = slab - b * g.Nh;
+
+    int l = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k)
+        if (job >= tp.job_begin[k] && job < tp.job_begin[k + 1]) l = k;
+    const LevelTiles t = level_tiles(g, tp, l);
+    const int local = job - t.job0;
+    const int band = local / t.nch, chunk = local - band * t.nch;
+    const int kr = band / t.nbc, kc = band - kr * t.nbc;
+    const int r0 = kr * t.R, r1 = min(t.H, r0 + t.R);
+    const int c0 = kc * t.CW, c1 = min(t.W, c0 + t.CW);
+    const int tw = c1 - c0, th = r1 - r0, P = tw * th;
+    const int nbw = tw + 1;                  // anchor bins cover rows r0-1..r1-1, cols c0-1..c1-1
+    const int nbins = (th + 1) * nbw;
+    const int sb = slab * tp.bands + t.band0 + band;
+    const int n = w.cnt[sb], o = w.off[slab * (tp.bands + 1) + t.band0 + band];
+    const int e_begin = o + (int)((int64_t)n * chunk / t.nch), e_end = o + (int)((int64_t)n * (chunk + 1) / t.nch);
+    const size_t lbase = (size_t)slab * tp.cap;
+    const float* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
+    const int gq = g.Nh * g.Ch;
+
+    const int grp = tid / LPU, lig = tid % LPU;
+    const int ch = lig * 4;
+    const bool lane_ok = ch < g.Ch;
+    const float* gl = grow0 + ch;
+
+    float4 acc[PPG];
+#pragma unroll
+    for (int m = 0; m < PPG; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    for (int p0 = e_begin; p0 < e_end; p0 += E) {
+        const int m_cnt = min(E, e_end - p0);
+        // stage a pass of list entries and count them per anchor bin
+        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < m_cnt; i += kTileBlock) {
+            const size_t pos = lbase + p0 + i;
+            int x0, y0;
+            unpack_anchor(w.anchor[pos], x0, y0);
+            const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
+            const int q = (int)w.k[pos] / g.Np;
+            s_ent[i] = make_float4(w.fx[pos], w.fy[pos], w.a[pos], __int_as_float(q));
+            s_bin_of[i] = (uint16_t)bin;
+            atomicAdd(&s_cursor[bin], 1);
+        }
+        __syncthreads();
+        // exclusive scan of the bin counts
+        for (int base = 0; base < nbins; base += kTileBlock) {
+            const int i = base + tid;
+            const int v = i < nbins ? s_cursor[i] : 0;
+            int incl = v;
+            const int lane = tid % kWave, wave = tid / kWave;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int u = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += u;
+            }
+            if (lane == kWave - 1) s_wave[wave] = incl;
+            __syncthreads();
+            int before = base == 0 ? 0 : s_bstart[base];
+            for (int ww = 0; ww < wave; ++ww) before += s_wave[ww];
+            if (i < nbins) s_bstart[i] = before + incl - v;
+            if (tid == kTileBlock - 1) {
+                int tot = base == 0 ? 0 : s_bstart[base];
+                for (int ww = 0; ww < kWaves; ++ww) tot += s_wave[ww];
+                s_bstart[min(base + kTileBlock, nbins)] = tot;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
+        __syncthreads();
+        for (int i = tid; i < m_cnt; i += kTileBlock) s_sorted[atomicAdd(&s_cursor[s_bin_of[i]], 1)] = (uint16_t)i;
+        __syncthreads();
+        // every pixel group sums its pixels' four neighbouring bins; partial sums
+        // per bin keep float32 rounding chains short
+        if (lane_ok) {
+#pragma unroll
+            for (int m = 0; m < PPG; ++m) {
+                const int p = grp + m * NG;
+                if (p >= P) break;
+                const int py = p / tw, px = p - py * tw;
+                float4 pix = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+                for (int corner = 0; corner < 4; ++corner) {
+                    const int dx = corner & 1, dy = corner >> 1;
+                    const int bin = (py + 1 - dy) * nbw + (px + 1 - dx);
+                    const int e1 = s_bstart[bin + 1];
+                    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int e = s_bstart[bin]; e < e1; e += 4) {
+                        float4 ent[4], gv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            ent[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                            gv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                            if (e + u < e1) {
+                                ent[u] = s_ent[s_sorted[e + u]];
+                                gv[u] = *reinterpret_cast<const float4*>(gl + __float_as_int(ent[u].w) * gq);
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float wx = dx ? ent[u].x : 1.f - ent[u].x;
+                            const float wy = dy ? ent[u].y : 1.f - ent[u].y;
+                            const float coef = ent[u].z * (wx * wy);
+                            sum.x = __builtin_fmaf(coef, gv[u].x, sum.x);
+                            sum.y = __builtin_fmaf(coef, gv[u].y, sum.y);
+                            sum.z = __builtin_fmaf(coef, gv[u].z, sum.z);
+                            sum.w = __builtin_fmaf(coef, gv[u].w, sum.w);
+                        }
+                    }
+                    pix.x += sum.x;
+                    pix.y += sum.y;
+                    pix.z += sum.z;
+                    pix.w += sum.w;
+                }
+                acc[m].x += pix.x;
+                acc[m].y += pix.y;
+                acc[m].z += pix.z;
+                acc[m].w += pix.w;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Write the tile: one workgroup per band stores; bands split over several
+    // chunks are added into the cleared grad_value.
+    if (!lane_ok) return;
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    float* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride + ch;
+#pragma unroll
+    for (int m = 0; m < PPG; ++m) {
+        const int p = grp + m * NG;
+        if (p >= P) break;
+        const int py = p / tw, px = p - py * tw;
+        float* dst = out + ((r0 + py) * t.W + c0 + px) * pstride;
+        if (t.nch == 1) {
+            *reinterpret_cast<float4*>(dst) = acc[m];
+        } else {
+            if (acc[m].x != 0.f) unsafeAtomicAdd(dst + 0, acc[m].x);
+            if (acc[m].y != 0.f) unsafeAtomicAdd(dst + 1, acc[m].y);
+            if (acc[m].z != 0.f) unsafeAtomicAdd(dst + 2, acc[m].z);
+            if (acc[m].w != 0.f) unsafeAtomicAdd(dst + 3, acc[m].w);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic path: any C_h, any alignment. One channel per lane (LPU lanes per
+// unit, channels beyond LPU in a loop); grad_value via float atomics.
+template <int LPU>
+__global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, int sc_max,
+                                                                  const float* __restrict__ grad_out,
+                                                                  const float* __restrict__ value,
+                                                                  const float* __restrict__ loc,
+                                                                  const float* __restrict__ attn,
+                                                                  float* __restrict__ grad_value,
+                                                                  float* __restrict__ grad_loc,
+                                                                  float* __restrict__ grad_attn)
 {
     constexpr int upb = kBlock / LPU;
     extern __shared__ float4 smem[];
     const int row = sc_max + 1;
     BwdRecord* s_rec = reinterpret_cast<BwdRecord*>(smem);
-    float4* s_res = smem + (upb * row * sizeof(BwdRecord)) / sizeof(float4);  // (gA, gx, gy, -)
+    float4* s_res = smem + 2 * upb * row;
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
-    const int S = g.S;
-    const int plane = g.Nq * g.Nh * S;
-
-    const int grp = tid / LPU;
-    const int lig = tid % LPU;
-    const int u = u0 + grp;
-    const bool unit_ok = u < g.units;
-    const int uc = unit_ok ? u : 0;  // tail lanes: keep every address in range
-    const int q = uc % g.Nq;
-    const int bh = uc / g.Nq;
-    const int h = bh % g.Nh, b = bh / g.Nh;
-    const int c0 = lig * VEC;
-    const int cstep = LPU * VEC;
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    const int slab_off = g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch;
-    const float* vslab = value + slab_off;
-    float* gslab = grad_value ? grad_value + slab_off : nullptr;
-    const float* grow = grad_out + ((b * g.Nq + q) * g.Nh + h) * g.Ch;
     const bool want_dots = grad_loc != nullptr || grad_attn != nullptr;
 
-    // grad_output of the first channel chunk stays in registers
-    float G0[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) G0[i] = 0.f;
-    if (unit_ok && c0 < g.Ch) VecIO<float, VEC>::load(grow + c0, G0);
+    const int grp = tid / LPU, lig = tid % LPU;
+    const int u = u0 + grp;
+    const bool unit_ok = u < g.units;
+    const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    const int slab_off = value_slab_offset(g, ui.b, ui.h);
+    const float* vslab = value + slab_off;
+    float* gslab = grad_value ? grad_value + slab_off : nullptr;
+    const float* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
+    const AnchorWs no_ws = {nullptr, nullptr, nullptr, nullptr};
 
-    for (int s0 = 0; s0 < S; s0 += sc_max) {
-        const int sc = min(sc_max, S - s0);
+    for (int s0 = 0; s0 < g.S; s0 += sc_max) {
+        const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
-        // ---- stage one record per (unit, sample) ----
-        for (int i = tid; i < upb * sc; i += kBlock) {
-            const int gi = i / sc;
-            const int s = i - gi * sc;
-            const int uu = u0 + gi;
-            BwdRecord r = {0.f, 0.f, 0.f, 0.f, 0, 1, 0, 0.f};
-            if (uu < g.units) {
-                const int qq = uu % g.Nq;
-                const int t = uu / g.Nq;
-                const int hh = t % g.Nh, bb = t / g.Nh;
-                const int si = s0 + s;
-                const int l = si / g.Np;
-                int H, W, start;
-                level_of(g.lv, l, H, W, start);
-                const int idx = ((bb * g.Nq + qq) * g.Nh + hh) * S + si;
-                float ux, uy;
-                if (g.b2q) {
-                    const int j = bb * 2 * plane + (qq * g.Nh + hh) * S + si;
-                    ux = loc[j];
-                    uy = loc[j + plane];
-                } else if (g.loc_pair_aligned) {
-                    const float2 xy = *reinterpret_cast<const float2*>(loc + 2 * idx);
-                    ux = xy.x; uy = xy.y;
-                } else {
-                    ux = loc[2 * idx];
-                    uy = loc[2 * idx + 1];
-                }
-                float x = pixel_coord(ux, W, g.align_corners);
-                float y = pixel_coord(uy, H, g.align_corners);
-                float kx = g.align_corners ? (float)(W - 1) : (float)W;
-                float ky = g.align_corners ? (float)(H - 1) : (float)H;
-                if (g.border) {
-                    if (!(x >= 0.f)) { x = 0.f; kx = 0.f; }                        // also NaN
-                    else if (x > (float)(W - 1)) { x = (float)(W - 1); kx = 0.f; }
-                    if (!(y >= 0.f)) { y = 0.f; ky = 0.f; }
-                    else if (y > (float)(H - 1)) { y = (float)(H - 1); ky = 0.f; }
-                } else {
-                    x = fminf(fmaxf(x, -2.f), (float)(W + 1));
-                    y = fminf(fmaxf(y, -2.f), (float)(H + 1));
-                }
-                const float x0f = floorf(x), y0f = floorf(y);
-                const int x0 = (int)x0f, y0 = (int)y0f;
-                const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
-                const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
-                r.fx = x - x0f;
-                r.fy = y - y0f;
-                r.kx = kx;
-                r.ky = ky;
-                r.pix = start + y0 * W + x0;
-                r.W = W;
-                r.mask = (ix0 && iy0 ? 1 : 0) | (ix1 && iy0 ? 2 : 0) | (ix0 && iy1 ? 4 : 0) | (ix1 && iy1 ? 8 : 0);
-                r.a = attn[idx];
-            }
-            s_rec[gi * row + s] = r;
-        }
+        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, no_ws);
         __syncthreads();
-        // ---- re-gather, three reductions, scatter ----
         if (unit_ok) {
-            const BwdRecord* rr = s_rec + grp * row;
             for (int s = 0; s < sc; ++s) {
-                const BwdRecord r = rr[s];
+                const BwdRecord r = s_rec[grp * row + s];
                 const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
                 const float w00 = gxw * gyw, w01 = r.fx * gyw, w10 = gxw * r.fy, w11 = r.fx * r.fy;
                 const int o00 = r.pix * pstride;
@@ -173,41 +706,26 @@ __global__ __launch_bounds__(kBlock) void backward_kernel(Geometry g, int sc_max
                 const int o10 = o00 + r.W * pstride;
                 const int o11 = o10 + pstride;
                 float pa = 0.f, px = 0.f, py = 0.f;
-                for (int c = c0; c < g.Ch; c += cstep) {
-                    if (!want_dots && !gslab) break;
-                    float G[VEC], v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-                    if (c == c0) {
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) G[i] = G0[i];
-                    } else {
-                        VecIO<float, VEC>::load(grow + c, G);
-                    }
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) { v00[i] = 0.f; v01[i] = 0.f; v10[i] = 0.f; v11[i] = 0.f; }
-                    if (r.mask & 1) VecIO<float, VEC>::load(vslab + o00 + c, v00);
-                    if (r.mask & 2) VecIO<float, VEC>::load(vslab + o01 + c, v01);
-                    if (r.mask & 4) VecIO<float, VEC>::load(vslab + o10 + c, v10);
-                    if (r.mask & 8) VecIO<float, VEC>::load(vslab + o11 + c, v11);
+                for (int c = lig; c < g.Ch; c += LPU) {
+                    const float Gc = grow[c];
                     if (want_dots) {
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) {
-                        const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
-                        const float dx = gyw * (v01[i] - v00[i]) + r.fy * (v11[i] - v10[i]);
-                        const float dy = gxw * (v10[i] - v00[i]) + r.fx * (v11[i] - v01[i]);
-                        pa = __builtin_fmaf(G[i], smp, pa);
-                        px = __builtin_fmaf(G[i], dx, px);
-                        py = __builtin_fmaf(G[i], dy, py);
-                    }
+                        const float v00 = (r.mask & 1) ? vslab[o00 + c] : 0.f;
+                        const float v01 = (r.mask & 2) ? vslab[o01 + c] : 0.f;
+                        const float v10 = (r.mask & 4) ? vslab[o10 + c] : 0.f;
+                        const float v11 = (r.mask & 8) ? vslab[o11 + c] : 0.f;
+                        const float smp = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
+                        const float dx = gyw * (v01 - v00) + r.fy * (v11 - v10);
+                        const float dy = gxw * (v10 - v00) + r.fx * (v11 - v01);
+                        pa = __builtin_fmaf(Gc, smp, pa);
+                        px = __builtin_fmaf(Gc, dx, px);
+                        py = __builtin_fmaf(Gc, dy, py);
                     }
                     if (gslab) {
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) {
-                            const float ag = r.a * G[i];
-                            if (r.mask & 1) unsafeAtomicAdd(gslab + o00 + c + i, ag * w00);
-                            if (r.mask & 2) unsafeAtomicAdd(gslab + o01 + c + i, ag * w01);
-                            if (r.mask & 4) unsafeAtomicAdd(gslab + o10 + c + i, ag * w10);
-                            if (r.mask & 8) unsafeAtomicAdd(gslab + o11 + c + i, ag * w11);
-                        }
+                        const float ag = r.a * Gc;
+                        if (r.mask & 1) unsafeAtomicAdd(gslab + o00 + c, ag * w00);
+                        if (r.mask & 2) unsafeAtomicAdd(gslab + o01 + c, ag * w01);
+                        if (r.mask & 4) unsafeAtomicAdd(gslab + o10 + c, ag * w10);
+                        if (r.mask & 8) unsafeAtomicAdd(gslab + o11 + c, ag * w11);
                     }
                 }
                 if (want_dots) {
@@ -220,50 +738,12 @@ __global__ __launch_bounds__(kBlock) void backward_kernel(Geometry g, int sc_max
         }
         if (!want_dots) continue;
         __syncthreads();
-        // ---- coalesced stores of grad_A and grad_loc for this chunk ----
-        for (int i = tid; i < upb * sc; i += kBlock) {
-            const int gi = i / sc;
-            const int s = i - gi * sc;
-            const int uu = u0 + gi;
-            if (uu >= g.units) continue;
-            const int qq = uu % g.Nq;
-            const int t = uu / g.Nq;
-            const int hh = t % g.Nh, bb = t / g.Nh;
-            const int si = s0 + s;
-            const int idx = ((bb * g.Nq + qq) * g.Nh + hh) * S + si;
-            const float4 res = s_res[gi * row + s];
-            if (grad_attn) grad_attn[idx] = res.x;
-            if (grad_loc) {
-                if (g.b2q) {
-                    const int j = bb * 2 * plane + (qq * g.Nh + hh) * S + si;
-                    grad_loc[j] = res.y;
-                    grad_loc[j + plane] = res.z;
-                } else if (g.loc_pair_aligned) {
-                    *reinterpret_cast<float2*>(grad_loc + 2 * idx) = make_float2(res.y, res.z);
-                } else {
-                    grad_loc[2 * idx] = res.y;
-                    grad_loc[2 * idx + 1] = res.z;
-                }
-            }
-        }
+        store_results(g, s_res, row, u0, upb, s0, sc, grad_loc, grad_attn);
     }
 }
 
-template <int VEC, int LPU>
-static hipError_t launch_backward_t(const Geometry& g, const float* grad_out, const float* value,
-                                    const float* loc, const float* attn, float* grad_value,
-                                    float* grad_loc, float* grad_attn, hipStream_t stream)
-{
-    constexpr int upb = kBlock / LPU;
-    static_assert(sizeof(BwdRecord) % sizeof(float4) == 0, "records must tile float4 slots");
-    const size_t per = sizeof(BwdRecord) + sizeof(float4);  // staged record + result slot
-    int sc = g.S < 16 ? g.S : 16;
-    while (sc > 1 && (size_t)upb * (sc + 1) * per > kLdsBudget) --sc;
-    const size_t lds = (size_t)upb * (sc + 1) * per;
-    hipLaunchKernelGGL((backward_kernel<VEC, LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                       grad_out, value, loc, attn, grad_value, grad_loc, grad_attn);
-    return hipGetLastError();
-}
+// ---------------------------------------------------------------------------
+// host launchers
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream)
 {
@@ -282,21 +762,141 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_backward(const Geometry& g, int vec, int lpu, const float* grad_out, const float* value,
-                           const float* loc, const float* attn, float* grad_value, float* grad_loc,
-                           float* grad_attn, hipStream_t stream)
+static int samples_per_chunk(int S, int upb)
 {
-#define MSDA_BWD_CASE(V, P)                                                                       \
-    if (vec == V && lpu == P)                                                                     \
-        return launch_backward_t<V, P>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    MSDA_BWD_CASE(1, 1) MSDA_BWD_CASE(1, 2) MSDA_BWD_CASE(1, 4) MSDA_BWD_CASE(1, 8)
-    MSDA_BWD_CASE(1, 16) MSDA_BWD_CASE(1, 32) MSDA_BWD_CASE(1, 64)
-    MSDA_BWD_CASE(2, 1) MSDA_BWD_CASE(2, 2) MSDA_BWD_CASE(2, 4) MSDA_BWD_CASE(2, 8)
-    MSDA_BWD_CASE(2, 16) MSDA_BWD_CASE(2, 32) MSDA_BWD_CASE(2, 64)
-    MSDA_BWD_CASE(4, 1) MSDA_BWD_CASE(4, 2) MSDA_BWD_CASE(4, 4) MSDA_BWD_CASE(4, 8)
-    MSDA_BWD_CASE(4, 16) MSDA_BWD_CASE(4, 32) MSDA_BWD_CASE(4, 64)
-#undef MSDA_BWD_CASE
-    return hipErrorInvalidValue;
+    const size_t per = sizeof(BwdRecord) + sizeof(float4);  // staged record + result slot
+    int sc = S < 16 ? S : 16;
+    while (sc > 1 && (size_t)upb * (sc + 1) * per > kLdsBudget) --sc;
+    return sc;
+}
+
+template <int LPU>
+static hipError_t launch_fast_t(const Geometry& g, const float* grad_out, const float* value, const float* loc,
+                                const float* attn, float* grad_loc, float* grad_attn, AnchorWs ws,
+                                hipStream_t stream)
+{
+    constexpr int upb = kBlock / LPU;
+    const int sc = samples_per_chunk(g.S, upb);
+    const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
+    hipLaunchKernelGGL((backward_fast_kernel<LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc, grad_out,
+                       value, loc, attn, grad_loc, grad_attn, ws);
+    return hipGetLastError();
+}
+
+template <int LPU>
+static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const float* grad_out,
+                                 float* grad_value, hipStream_t stream)
+{
+    const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
+    hipLaunchKernelGGL((tile_scatter_kernel<LPU>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g, tp, w,
+                       grad_out, grad_value);
+    return hipGetLastError();
+}
+
+template <int LPU>
+static hipError_t launch_generic_t(const Geometry& g, const float* grad_out, const float* value,
+                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
+                                   float* grad_attn, hipStream_t stream)
+{
+    constexpr int upb = kBlock / LPU;
+    const int sc = samples_per_chunk(g.S, upb);
+    const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
+    hipLaunchKernelGGL((backward_generic_kernel<LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                       grad_out, value, loc, attn, grad_value, grad_loc, grad_attn);
+    return hipGetLastError();
+}
+
+// Workspace of the fast path with grad_value: per-sample arrays (16 bytes per
+// sample), band counts / cursors / offsets, and the band lists (20 bytes per
+// reserved entry). Every piece starts 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws)
+{
+    const size_t ns = (size_t)g.B * g.Nh * g.Nq * g.S;
+    const size_t slabs = (size_t)g.B * g.Nh;
+    const size_t nb = (size_t)tp.bands;
+    const size_t cap = (size_t)tp.cap * slabs;
+    size_t at = 0;
+    char* p = static_cast<char*>(base);
+    auto take = [&](size_t bytes) {
+        char* r = p ? p + at : nullptr;
+        at = align256(at + bytes);
+        return r;
+    };
+    AnchorWs a;
+    a.anchor = reinterpret_cast<uint32_t*>(take(ns * 4));
+    a.fx = reinterpret_cast<float*>(take(ns * 4));
+    a.fy = reinterpret_cast<float*>(take(ns * 4));
+    a.a = reinterpret_cast<float*>(take(ns * 4));
+    BandWs w;
+    w.cnt = reinterpret_cast<int*>(take(slabs * nb * 4 * 2));  // counts, then cursors
+    w.cursor = w.cnt ? w.cnt + slabs * nb : nullptr;
+    w.off = reinterpret_cast<int*>(take(slabs * (nb + 1) * 4));
+    w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
+    w.anchor = reinterpret_cast<uint32_t*>(take(cap * 4));
+    w.fx = reinterpret_cast<float*>(take(cap * 4));
+    w.fy = reinterpret_cast<float*>(take(cap * 4));
+    w.a = reinterpret_cast<float*>(take(cap * 4));
+    if (aws) *aws = a;
+    if (bws) *bws = w;
+    return at;
+}
+
+// Fast path. grad_value (if any) must already be cleared when tp.any_chunked.
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, const float* grad_out,
+                                const float* value, const float* loc, const float* attn, float* grad_value,
+                                float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream)
+{
+    AnchorWs ws = {nullptr, nullptr, nullptr, nullptr};
+    BandWs bw = {};
+    if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw);
+    hipError_t e;
+    switch (lpu) {
+    case 1: e = launch_fast_t<1>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
+    case 2: e = launch_fast_t<2>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
+    case 4: e = launch_fast_t<4>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
+    case 8: e = launch_fast_t<8>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
+    case 16: e = launch_fast_t<16>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || !grad_value) return e;
+    const int slabs = g.B * g.Nh;
+    // bucket the samples by band
+    e = launch_zero(reinterpret_cast<float*>(bw.cnt), (int64_t)slabs * tp.bands * 2, stream);
+    if (e != hipSuccess) return e;
+    const dim3 bgrid((g.Nq * g.Np + kBandChunk - 1) / kBandChunk, g.Nl, slabs);
+    hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
+    hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
+    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, bw, ws.anchor, ws.fx, ws.fy,
+                       ws.a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (lpu) {
+    case 1: return launch_tiles_t<1>(g, tp, bw, grad_out, grad_value, stream);
+    case 2: return launch_tiles_t<2>(g, tp, bw, grad_out, grad_value, stream);
+    case 4: return launch_tiles_t<4>(g, tp, bw, grad_out, grad_value, stream);
+    case 8: return launch_tiles_t<8>(g, tp, bw, grad_out, grad_value, stream);
+    case 16: return launch_tiles_t<16>(g, tp, bw, grad_out, grad_value, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Generic path. grad_value (if any) must already be cleared.
+hipError_t launch_backward_generic(const Geometry& g, int lpu, const float* grad_out, const float* value,
+                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
+                                   float* grad_attn, hipStream_t stream)
+{
+    switch (lpu) {
+    case 1: return launch_generic_t<1>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 2: return launch_generic_t<2>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 4: return launch_generic_t<4>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 8: return launch_generic_t<8>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 16: return launch_generic_t<16>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 32: return launch_generic_t<32>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    case 64: return launch_generic_t<64>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace msda

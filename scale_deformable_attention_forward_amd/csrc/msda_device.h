@@ -37,6 +37,32 @@ struct Geometry {
     Levels lv;
 };
 
+// Destination-tiled grad_value pass (backward). Every level is cut into
+// bands (tiles) of `rows` x `cols` pixels. Samples are bucketed by the bands
+// their 2x2 corner block touches into one contiguous list per (b, h, band);
+// a tile job is (band, chunk of that band's list).
+constexpr int kTileBlock = 512;          // threads per tile workgroup
+constexpr int kTilePixelsPerGroup = 8;   // destination pixels owned by one lane group
+constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
+constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
+constexpr int kBandBlock = 256;          // threads of the bucketing kernels
+constexpr int kBandChunk = 4096;         // samples per bucketing workgroup
+constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
+
+struct TilePlan {
+    int32_t jobs;                        // tile jobs per (b, h) slab
+    int32_t bands;                       // bands per slab
+    int32_t any_chunked;                 // some band is split over chunks (atomic flush)
+    int64_t cap;                         // list entries reserved per slab
+    int32_t rows[kMaxLevels];
+    int32_t row_bands[kMaxLevels];
+    int32_t cols[kMaxLevels];
+    int32_t col_bands[kMaxLevels];
+    int32_t chunks[kMaxLevels];
+    int32_t band_begin[kMaxLevels];      // first band of level l within the slab
+    int32_t job_begin[kMaxLevels + 1];
+};
+
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).
 // Renumber them so that each XCD receives one contiguous range of logical
 // blocks: consecutive logical blocks share a (b, h) slab of value, so each

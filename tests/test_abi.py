@@ -138,11 +138,31 @@ def test_backward_bf16_not_implemented(lib):
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 4
 
 
-def test_workspace_size_fp32_is_zero(lib):
+def test_workspace_size(lib):
+    # C_h = 8: the tiled grad_value pass needs per-sample anchors plus band lists
     prob, keep = _prob()
     sz = ctypes.c_size_t(123)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
+    assert sz.value >= 16 * (1 * 5 * 2 * 2 * 2) and sz.value % 256 == 0
+    # C_h = 6 takes the generic path: no workspace
+    prob, keep = _prob(C_h=6)
+    assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
     assert sz.value == 0
+
+
+def test_workspace_too_small(lib):
+    prob, keep = _prob()
+    ws = ctypes.c_void_p(0x90_0000_0000)
+    code = lib.msda_backward(ctypes.byref(prob), P["gout"], P["value"], P["loc"], P["attn"], P["gv"],
+                             P["gl"], P["ga"], ws, 16, None)
+    assert code == 5
+    code = lib.msda_backward(ctypes.byref(prob), P["gout"], P["value"], P["loc"], P["attn"], P["gv"],
+                             P["gl"], P["ga"], None, 0, None)
+    assert code == 5
+    # a workspace overlapping an input is rejected
+    code = lib.msda_backward(ctypes.byref(prob), P["gout"], P["value"], P["loc"], P["attn"], P["gv"],
+                             P["gl"], P["ga"], P["value"], 1 << 20, None)
+    assert code == 1
 
 
 def test_empty_forward_is_noop(lib):

@@ -249,3 +249,18 @@ def test_autograd_function_matches_oracle(gpu_device):
     compare("autograd grad_value", to_numpy(v.grad), gv, RTOL["fp32"])
     compare("autograd grad_loc", to_numpy(loc.grad), gl, RTOL["fp32"])
     compare("autograd grad_attn", to_numpy(a.grad), ga, RTOL["fp32"])
+
+
+@pytest.mark.parametrize("C_h,levels,N_q,N_p,B,N_h", [
+    (32, ((16, 20), (8, 10), (4, 5), (2, 3)), 2000, 4, 2, 2),  # several LDS-privatised levels and query chunks
+    (64, ((40, 40), (5, 5)), 3200, 4, 1, 1),                   # 64 channels: the big level in channel slices
+    (16, ((30, 30), (3, 3)), 1000, 8, 1, 3),
+    (8, ((12, 12),), 500, 4, 3, 1),
+    (12, ((9, 11), (2, 2)), 700, 3, 1, 2),                     # C_h not a power of two
+])
+def test_dense_coarse_levels(C_h, levels, N_q, N_p, B, N_h, gpu_device):
+    """Many samples per pixel: the coarse levels' grad_value goes through LDS."""
+    for vl, pad in (("BLNC", "zeros"), ("BNLC", "border")):
+        d = _mk(seed=18, levels=levels, N_q=N_q, N_p=N_p, B=B, N_h=N_h, C_h=C_h, value_layout=vl, pad=pad)
+        _check_backward(d, gpu_device, f"dense coarse C_h={C_h} {levels} {vl} {pad}")
+        _check_backward(d, gpu_device, f"dense coarse grad_value only C_h={C_h}", (True, False, False))
