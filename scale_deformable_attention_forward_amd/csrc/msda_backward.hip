@@ -435,32 +435,67 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
     if (tid == 0) o[n] = carry;
 }
 
-// Bucketing 3/3: fill the band lists. Grid as band_count_kernel; each
-// workgroup reserves one contiguous run per band it touches.
+// Bucketing 3/3: fill the band lists. Grid as band_count_kernel. Each
+// workgroup orders its entries by band in LDS, reserves one contiguous run
+// per band it touches, and writes every run with consecutive stores.
+// Dynamic LDS: 3 * (max_bands + 1) ints, then max_entries (k, band) pairs
+// (kBandChunk samples times the most bands one sample can touch).
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
                                                                const uint32_t* __restrict__ anchor,
                                                                const float* __restrict__ sfx,
                                                                const float* __restrict__ sfy,
-                                                               const float* __restrict__ sa)
+                                                               const float* __restrict__ sa, int max_bands,
+                                                               int max_entries)
 {
-    __shared__ int hist[kMaxBandsPerLevel];
-    __shared__ int base[kMaxBandsPerLevel];
+    constexpr int kWaves = kBandBlock / kWave;
+    extern __shared__ int dyn[];
+    int* hist = dyn;
+    int* base = hist + max_bands + 1;
+    int* loff = base + max_bands + 1;
+    uint32_t* s_k = reinterpret_cast<uint32_t*>(loff + max_bands + 1);
+    uint16_t* s_band = reinterpret_cast<uint16_t*>(s_k + max_entries);
+    __shared__ int s_wave[kWaves];
+    const int tid = threadIdx.x;
     const int l = blockIdx.y, slab = blockIdx.z;
     const LevelTiles t = level_tiles(g, tp, l);
     const int nb = t.nbr * t.nbc;
     const int nsamp = g.Nq * g.Np;
     const int k0 = blockIdx.x * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
-    for (int i = threadIdx.x; i < nb; i += kBandBlock) hist[i] = 0;
+    for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
     const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
-    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
+    for (int k = k0 + tid; k < k1; k += kBandBlock) {
         int x0, y0, bands[4];
         unpack_anchor(anchor[sbase + k], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
         for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += kBandBlock) {
+    // exclusive scan of hist[0..nb) into loff, in rounds of kBandBlock bands
+    const int lane = tid % kWave, wave = tid / kWave;
+    int carry = 0;
+    for (int r = 0; r < nb; r += kBandBlock) {
+        const int i = r + tid;
+        const int v = i < nb ? hist[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int u = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += u;
+        }
+        if (lane == kWave - 1) s_wave[wave] = incl;
+        __syncthreads();
+        int before = carry, total = carry;
+        for (int ww = 0; ww < kWaves; ++ww) {
+            before += ww < wave ? s_wave[ww] : 0;
+            total += s_wave[ww];
+        }
+        if (i < nb) loff[i] = before + incl - v;
+        carry = total;
+        __syncthreads();
+    }
+    if (tid == 0) loff[nb] = carry;
+    for (int i = tid; i < nb; i += kBandBlock) {
         if (hist[i]) {
             const int sb = slab * tp.bands + t.band0 + i;
             base[i] = w.off[slab * (tp.bands + 1) + t.band0 + i] + atomicAdd(&w.cursor[sb], hist[i]);
@@ -468,23 +503,35 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
         }
     }
     __syncthreads();
-    const size_t lbase = (size_t)slab * tp.cap;
-    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
-        const uint32_t an = anchor[sbase + k];
+    for (int k = k0 + tid; k < k1; k += kBandBlock) {
         int x0, y0, bands[4];
-        unpack_anchor(an, x0, y0);
+        unpack_anchor(anchor[sbase + k], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
-        if (n == 0) continue;
-        const float fx = sfx[sbase + k], fy = sfy[sbase + k], a = sa[sbase + k];
         for (int j = 0; j < n; ++j) {
-            const size_t pos = lbase + base[bands[j]] + atomicAdd(&hist[bands[j]], 1);
-            w.k[pos] = (uint32_t)k;
-            w.anchor[pos] = an;
-            w.fx[pos] = fx;
-            w.fy[pos] = fy;
-            w.a[pos] = a;
+            const int slot = loff[bands[j]] + atomicAdd(&hist[bands[j]], 1);
+            s_k[slot] = (uint32_t)k;
+            s_band[slot] = (uint16_t)bands[j];
         }
     }
+    __syncthreads();
+    const int total = loff[nb];
+    const size_t lbase = (size_t)slab * tp.cap;
+    for (int i = tid; i < total; i += kBandBlock) {
+        const int bnd = s_band[i];
+        const size_t pos = lbase + base[bnd] + (i - loff[bnd]);
+        const uint32_t k = s_k[i];
+        w.k[pos] = k;
+        w.anchor[pos] = anchor[sbase + k];
+        w.fx[pos] = sfx[sbase + k];
+        w.fy[pos] = sfy[sbase + k];
+        w.a[pos] = sa[sbase + k];
+    }
+}
+
+// Dynamic LDS bytes of band_fill_kernel.
+static size_t band_fill_lds(int max_bands, int max_entries)
+{
+    return (size_t)3 * (max_bands + 1) * sizeof(int) + (size_t)max_entries * (sizeof(uint32_t) + sizeof(uint16_t));
 }
 
 // Tile kernel. LPU lanes per destination pixel (4 channels per lane),
@@ -868,8 +915,20 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
     const dim3 bgrid((g.Nq * g.Np + kBandChunk - 1) / kBandChunk, g.Nl, slabs);
     hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
     hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
-    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, bw, ws.anchor, ws.fx, ws.fy,
-                       ws.a);
+    int max_bands = 1, max_mult = 2;
+    for (int l = 0; l < g.Nl; ++l) {
+        max_bands = std::max(max_bands, tp.row_bands[l] * tp.col_bands[l]);
+        if (tp.col_bands[l] > 1) max_mult = 4;
+    }
+    const int max_entries = kBandChunk * max_mult;
+    const size_t fill_lds = band_fill_lds(max_bands, max_entries);
+    if (fill_lds > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&band_fill_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)fill_lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), fill_lds, stream, g, tp, bw, ws.anchor, ws.fx,
+                       ws.fy, ws.a, max_bands, max_entries);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (lpu) {

@@ -46,7 +46,7 @@ constexpr int kTilePixelsPerGroup = 8;   // destination pixels owned by one lane
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
 constexpr int kBandBlock = 256;          // threads of the bucketing kernels
-constexpr int kBandChunk = 4096;         // samples per bucketing workgroup
+constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
 
 struct TilePlan {
