@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with a 1 GiB scratch write between them (caches cold)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -122,6 +124,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.copy_calibration:
+        # a plain copy of known size: reads and writes 1 GiB per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": src.numel() * 4, "launches": 5}), flush=True)
+        return
     from scale_deformable_attention_forward_amd import binding
     from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_workload
 
@@ -138,6 +149,7 @@ def main():
     gl = torch.empty_like(loc)
     ga = torch.empty_like(attn)
     ss, ls = d["spatial_shapes"], d["level_start_index"]
+    ws = torch.empty(max(1, binding.backward_workspace_bytes(v, ss, ls, loc)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fwd():
@@ -145,7 +157,7 @@ def main():
 
     def bwd():
         binding.msda_backward(gout, v, ss, ls, loc, attn, grad_value=gv, grad_sampling_locations=gl,
-                              grad_attention_weights=ga, stream=stream)
+                              grad_attention_weights=ga, workspace=ws, stream=stream)
 
     for _ in range(a.warmup):
         fwd()

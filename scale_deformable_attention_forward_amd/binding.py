@@ -185,7 +185,7 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
                   align_corners=False, padding_mode="zeros", compute_grad_value=True,
                   compute_grad_sampling_locations=True, compute_grad_attention_weights=True,
                   grad_value=None, grad_sampling_locations=None, grad_attention_weights=None,
-                  stream=None):
+                  workspace=None, stream=None):
     """Backward: returns (grad_value, grad_sampling_locations, grad_attention_weights), each in
     its input's layout, with None in the slots whose compute flag is False."""
     lib = load_library()
@@ -222,12 +222,18 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
     st = lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(ws_bytes))
     _raise_for(lib, st, "msda_backward_workspace_size")
     ws = None
-    if ws_bytes.value:
-        ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=value.device)
+    if ws_bytes.value and gv is not None:
+        if workspace is not None:
+            if workspace.device != value.device or workspace.numel() * workspace.element_size() < ws_bytes.value:
+                raise ValueError(f"workspace must be a GPU tensor of at least {ws_bytes.value} bytes")
+            ws = workspace
+        else:
+            ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=value.device)
     ptr = (lambda t: None if t is None else t.data_ptr())
+    ws_len = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib.msda_backward(ctypes.byref(prob), grad_output.data_ptr(), value.data_ptr(),
                            sampling_locations.data_ptr(), attention_weights.data_ptr(), ptr(gv),
-                           ptr(gl), ptr(ga), ptr(ws), ws_bytes.value, _stream_ptr(stream))
+                           ptr(gl), ptr(ga), ptr(ws), ws_len, _stream_ptr(stream))
     _raise_for(lib, st, "msda_backward")
     return gv, gl, ga
 
@@ -267,3 +273,19 @@ def ms_deformable_attention(value, spatial_shapes, level_start_index, sampling_l
     return MSDeformableAttention.apply(value, spatial_shapes, level_start_index, sampling_locations,
                                        attention_weights, value_layout, sampling_locations_layout,
                                        align_corners, padding_mode)
+
+
+def backward_workspace_bytes(value, spatial_shapes, level_start_index, sampling_locations,
+                             value_layout="BLNC", sampling_locations_layout="BQHLP2",
+                             align_corners=False, padding_mode="zeros"):
+    """Bytes of workspace msda_backward needs for these shapes (0 if none)."""
+    lib = load_library()
+    B, L, N_q, N_h, C_h, N_l, N_p = _dims(value, sampling_locations, value_layout,
+                                          sampling_locations_layout)
+    prob, keep = make_problem(B, L, N_q, N_h, C_h, spatial_shapes, level_start_index, N_p,
+                              value_layout, sampling_locations_layout, align_corners, padding_mode,
+                              value.dtype)
+    n = ctypes.c_size_t(0)
+    _raise_for(lib, lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
+               "msda_backward_workspace_size")
+    return n.value

@@ -683,24 +683,42 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     }
 
     // Write the tile: one workgroup per band stores; bands split over several
-    // chunks are added into the cleared grad_value.
-    if (!lane_ok) return;
+    // chunks are added into the cleared grad_value, one channel per lane
+    // through LDS so that every atomic instruction covers whole channel rows.
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    float* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride + ch;
+    float* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
+    if (t.nch == 1) {
+        if (!lane_ok) return;
 #pragma unroll
-    for (int m = 0; m < PPG; ++m) {
-        const int p = grp + m * NG;
-        if (p >= P) break;
-        const int py = p / tw, px = p - py * tw;
-        float* dst = out + ((r0 + py) * t.W + c0 + px) * pstride;
-        if (t.nch == 1) {
-            *reinterpret_cast<float4*>(dst) = acc[m];
-        } else {
-            if (acc[m].x != 0.f) unsafeAtomicAdd(dst + 0, acc[m].x);
-            if (acc[m].y != 0.f) unsafeAtomicAdd(dst + 1, acc[m].y);
-            if (acc[m].z != 0.f) unsafeAtomicAdd(dst + 2, acc[m].z);
-            if (acc[m].w != 0.f) unsafeAtomicAdd(dst + 3, acc[m].w);
+        for (int m = 0; m < PPG; ++m) {
+            const int p = grp + m * NG;
+            if (p >= P) break;
+            const int py = p / tw, px = p - py * tw;
+            *reinterpret_cast<float4*>(out + ((r0 + py) * t.W + c0 + px) * pstride + ch) = acc[m];
         }
+        return;
+    }
+    float* stage = reinterpret_cast<float*>(s_ent);  // E float4 of staging
+    const int ppr = (E * 4) / g.Ch;                  // pixels per staging round
+    for (int q0 = 0; q0 < P; q0 += ppr) {
+        const int q1 = min(P, q0 + ppr);
+        if (lane_ok) {
+#pragma unroll
+            for (int m = 0; m < PPG; ++m) {
+                const int p = grp + m * NG;
+                if (p >= q0 && p < q1) *reinterpret_cast<float4*>(stage + (p - q0) * g.Ch + ch) = acc[m];
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < (q1 - q0) * g.Ch; i += kTileBlock) {
+            const float v = stage[i];
+            if (v != 0.f) {
+                const int pp = q0 + i / g.Ch, c = i - (i / g.Ch) * g.Ch;
+                const int yy = pp / tw, xx = pp - yy * tw;
+                unsafeAtomicAdd(out + ((r0 + yy) * t.W + c0 + xx) * pstride + c, v);
+            }
+        }
+        __syncthreads();
     }
 }
 
