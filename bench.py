@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fp32_fwd_bwd_hbm_traffic.txt")
 METRIC = "queries/s and effective gathered HBM GB/s (% of peak), fwd+bwd, 1 MI355X"
 WORKLOAD_NUM = 5                # encoder shapes with grad_output (the forward uses the same arrays)
 
@@ -92,6 +93,33 @@ def byte_counts(d):
                      "counted": 2 * inr * corner_bytes + bwd_streams},
         "queries": B * N_q,
     }
+
+
+def measured_traffic():
+    """HBM bytes per forward launch and per backward call, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by its copy calibration;
+    None for both when a kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None, None
+    for rel, digest in rec["sources_sha256"].items():
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
+            return None, None
+    ff = rec["copy_calibration"]["fetch_factor"]
+    wf = rec["copy_calibration"]["write_factor"]
+    fwd = bwd = 0.0
+    for name, c in rec["per_dispatch"].items():
+        b = (c["FETCH_SIZE_KiB"] * ff + c["WRITE_SIZE_KiB"] * wf) * 1024.0
+        if name.startswith("forward_kernel"):
+            fwd += b
+        elif name.startswith("zero4_kernel"):
+            bwd += 2 * b   # the backward clears its band counters and grad_value
+        else:
+            bwd += b
+    return fwd, bwd
 
 
 def cpu_baseline(d, target_s):
@@ -219,14 +247,21 @@ def main():
         }
 
     kf, kb = kernel_line("forward", f_ms), kernel_line("backward", b_ms)
+    t_fwd, t_bwd = measured_traffic()
+    kf["traffic"], kb["traffic"] = t_fwd, t_bwd
+    kf["launch"] = "forward_kernel (1 launch)"
+    kb["launch"] = ("msda_backward call: backward_fast_kernel, zero4_kernel x2, band_count_kernel, "
+                    "band_scan_kernel, band_fill_kernel, tile_scatter_kernel")
     dom_name, dom = ("backward", kb) if kb["ms_mean"] >= kf["ms_mean"] else ("forward", kf)
     achieved = dom["bytes_nominal"] / (dom["ms_mean"] * 1e-3) / 1e9
     roofline = {
         "bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        "frac": achieved / HBM_PEAK_GBS, "traffic": dom["traffic"],
         "bytes_per_launch": dom["bytes_nominal"],
-        "note": "algorithmic bytes = nominal per-query figure x queries (4 corners per sample); "
-                "achieved_counted uses in-range corners only",
+        "launch": dom["launch"],
+        "note": "achieved = algorithmic bytes (nominal per-query figure x queries, 4 corners per sample) "
+                "/ mean HIP-event time of one launch; achieved_counted uses in-range corners only; "
+                "traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles/)",
         "achieved_counted": dom["gbs_counted"],
     }
     res = {

@@ -117,12 +117,15 @@ msda_status msda_forward(const msda_problem* problem, const void* value,
                          void* output, hipStream_t stream);
 
 /*
- * Bytes of device workspace msda_backward needs for `problem` (0 when none):
- * 16 bytes per sample (B * N_q * N_h * N_l * N_p) when C_h % 4 == 0 and
- * C_h <= 64, which is the shape of the destination-tiled grad_value pass;
- * 0 otherwise. The workspace carries per-sample anchor corners, fractions and
- * attention weights between the two backward kernels; its contents are
- * scratch.
+ * Bytes of device workspace msda_backward needs for `problem` (0 when none).
+ * Non-zero only when C_h % 4 == 0 and C_h <= 64, the shape of the
+ * destination-tiled grad_value pass. It then holds, for S = B*N_q*N_h*N_l*N_p
+ * samples: 16 bytes per sample (anchor corner, fractions, attention weight),
+ * per-(batch, head, pixel band) counts and offsets, and band lists of 20 bytes
+ * per entry with room for 2 entries per sample (4 on levels wider than one
+ * band), each array rounded up to 256 bytes; about 320 MB for 2 x 22223
+ * queries, 8 heads, 4 levels, 4 points. The contents are scratch and need
+ * no initialisation.
  */
 msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* bytes);
 

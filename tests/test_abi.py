@@ -143,7 +143,9 @@ def test_workspace_size(lib):
     prob, keep = _prob()
     sz = ctypes.c_size_t(123)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
-    assert sz.value >= 16 * (1 * 5 * 2 * 2 * 2) and sz.value % 256 == 0
+    samples = 1 * 5 * 2 * 2 * 2
+    # 16 B per sample, plus band lists of 20 B per entry with 2 entries per sample
+    assert sz.value >= (16 + 2 * 20) * samples and sz.value % 256 == 0
     # C_h = 6 takes the generic path: no workspace
     prob, keep = _prob(C_h=6)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
