@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSDA_ABI_VERSION 1
+#define MSDA_ABI_VERSION 2
 #define MSDA_MAX_LEVELS 16
 
 typedef enum msda_status {
@@ -45,8 +45,7 @@ typedef enum msda_status {
     MSDA_ERR_INVALID_ARGUMENT = 1,  /* NULL/misaligned/overlapping pointer, bad size or enum */
     MSDA_ERR_INVALID_LEVELS = 2,    /* H or W < 1, L != sum H*W, starts not the prefix sums */
     MSDA_ERR_NOTHING_TO_COMPUTE = 3,/* backward with all three gradient outputs NULL */
-    MSDA_ERR_UNSUPPORTED = 4,       /* N_l > MSDA_MAX_LEVELS, a size past the index range,
-                                       or a dtype the call does not implement */
+    MSDA_ERR_UNSUPPORTED = 4,       /* N_l > MSDA_MAX_LEVELS or a size past the index range */
     MSDA_ERR_WORKSPACE_TOO_SMALL = 5,
     MSDA_ERR_HIP = 6                /* a HIP launch reported an error */
 } msda_status;
@@ -118,16 +117,24 @@ msda_status msda_forward(const msda_problem* problem, const void* value,
 
 /*
  * Bytes of device workspace msda_backward needs for `problem` (0 when none).
- * Non-zero only when C_h % 4 == 0 and C_h <= 64, the shape of the
- * destination-tiled grad_value pass. It then holds, for S = B*N_q*N_h*N_l*N_p
- * samples: 16 bytes per sample (anchor corner, fractions, attention weight),
- * per-(batch, head, pixel band) counts and offsets, and band lists of 20 bytes
- * per entry with room for 2 entries per sample (4 on levels wider than one
- * band), each array rounded up to 256 bytes; about 320 MB for 2 x 22223
- * queries, 8 heads, 4 levels, 4 points. The contents are scratch and need
- * no initialisation.
+ * The backward takes one of two paths per call:
+ *  - destination-tiled (C_h % 4 == 0, C_h <= 64, value / grad_output /
+ *    grad_value aligned to 4 elements, B * N_h <= 65535): for
+ *    S = B*N_q*N_h*N_l*N_p samples, 16 bytes per sample (anchor corner,
+ *    fractions, attention weight), per-(batch, head, pixel band) counts and
+ *    offsets, band lists of 20 bytes per entry with room for 2 entries per
+ *    sample (4 on levels wider than one band), and float32 partial tiles for
+ *    the bands of coarse levels that are split over several workgroups; about
+ *    390 MB for 2 x 22223 queries, 8 heads, 4 levels, 4 points, 32 channels;
+ *  - generic (any other shape or alignment): a float32 array of value's
+ *    element count for bfloat16, nothing for float32.
+ * The size returned covers both. The contents are scratch and need no
+ * initialisation.
  */
 msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* bytes);
+
+/* flags of msda_backward */
+#define MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE 1u  /* grad_value += result instead of = result */
 
 /*
  * Backward ("MS Deformable Attention Backward Kernel API Reference",
@@ -145,26 +152,32 @@ msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* by
  *   grad_value                same shape and layout as value, value_dtype, or NULL
  *   grad_sampling_locations   same shape and layout as sampling_locations, float32, or NULL
  *   grad_attention_weights    (B, N_q, N_h, N_l, N_p), float32, or NULL
+ *   flags                     0 or MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE (other
+ *                             bits: MSDA_ERR_INVALID_ARGUMENT)
  *   workspace, workspace_bytes: device memory, 16-byte aligned, at least
  *                             msda_backward_workspace_size bytes, not
- *                             overlapping any tensor (may be NULL/0 when that
- *                             size is 0 or grad_value is NULL); else
+ *                             overlapping any tensor (may be NULL/0 when
+ *                             grad_value is NULL); else
  *                             MSDA_ERR_WORKSPACE_TOO_SMALL
  *
  * A NULL gradient pointer skips that gradient (the compute_grad_* flags of the
  * page); all three NULL returns MSDA_ERR_NOTHING_TO_COMPUTE ("at least one
- * must be True"). Every non-NULL output is fully overwritten. grad_value is
- * computed per destination pixel: levels whose samples are spread over
- * several workgroups are finished with float32 atomic adds into a cleared
- * buffer, so their last bits may differ from run to run; grad_A and grad_loc
- * are deterministic. value_dtype must be MSDA_F32 (MSDA_ERR_UNSUPPORTED
- * otherwise).
+ * must be True"). grad_sampling_locations and grad_attention_weights are
+ * fully overwritten. grad_value is overwritten, or with
+ * MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE the result is added to what it holds
+ * (for bfloat16: one rounding of old + new); elements no sample reaches are
+ * written 0 (left as they are when accumulating). Sums are float32; a
+ * bfloat16 grad_value is rounded to nearest even once, at the end.
+ * Determinism: grad_A and grad_loc are bitwise reproducible; so is grad_value
+ * on the destination-tiled path (every element is the sum of its
+ * contributions in a fixed order); on the generic path grad_value is summed
+ * with float32 atomics and its last bits may differ from run to run.
  */
 msda_status msda_backward(const msda_problem* problem, const void* grad_output, const void* value,
                           const float* sampling_locations, const float* attention_weights,
                           void* grad_value, float* grad_sampling_locations,
-                          float* grad_attention_weights, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream);
+                          float* grad_attention_weights, unsigned int flags, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* msda_status_string(msda_status status);

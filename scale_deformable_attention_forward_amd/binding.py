@@ -30,6 +30,8 @@ VALUE_LAYOUTS = {"BLNC": 0, "BNLC": 1}
 LOC_LAYOUTS = {"BQHLP2": 0, "B2QHLP": 1}
 PADDINGS = {"zeros": 0, "border": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+ABI_VERSION = 2
+BACKWARD_ACCUMULATE_GRAD_VALUE = 1  # msda_backward flag: grad_value += result
 
 # Every symbol include/msda.h declares.
 EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
@@ -69,7 +71,7 @@ def load_library(path: str = LIB_PATH):
     pp = ctypes.POINTER(MsdaProblem)
     lib.msda_forward.argtypes = [pp, vp, vp, vp, vp, vp]
     lib.msda_forward.restype = ctypes.c_int
-    lib.msda_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msda_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward_workspace_size.argtypes = [pp, ctypes.POINTER(sz)]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
@@ -77,6 +79,9 @@ def load_library(path: str = LIB_PATH):
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
     lib.msda_abi_version.restype = ctypes.c_int
+    if lib.msda_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.msda_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}: rebuild the library")
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -185,9 +190,11 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
                   align_corners=False, padding_mode="zeros", compute_grad_value=True,
                   compute_grad_sampling_locations=True, compute_grad_attention_weights=True,
                   grad_value=None, grad_sampling_locations=None, grad_attention_weights=None,
-                  workspace=None, stream=None):
+                  accumulate_grad_value=False, workspace=None, stream=None):
     """Backward: returns (grad_value, grad_sampling_locations, grad_attention_weights), each in
-    its input's layout, with None in the slots whose compute flag is False."""
+    its input's layout, with None in the slots whose compute flag is False. With
+    ``accumulate_grad_value`` the given ``grad_value`` tensor is added to instead of
+    overwritten."""
     lib = load_library()
     B, L, N_q, N_h, C_h, N_l, N_p = _dims(value, sampling_locations, value_layout,
                                           sampling_locations_layout)
@@ -210,6 +217,8 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
             raise ValueError(f"{name} must have the shape of its input")
         return given
 
+    if accumulate_grad_value and compute_grad_value and grad_value is None:
+        raise ValueError("accumulate_grad_value needs a grad_value tensor to add to")
     gv = out(compute_grad_value, grad_value, value, value.dtype, "grad_value")
     gl = out(compute_grad_sampling_locations, grad_sampling_locations, sampling_locations,
              torch.float32, "grad_sampling_locations")
@@ -231,9 +240,10 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
             ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=value.device)
     ptr = (lambda t: None if t is None else t.data_ptr())
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
+    flags = BACKWARD_ACCUMULATE_GRAD_VALUE if accumulate_grad_value else 0
     st = lib.msda_backward(ctypes.byref(prob), grad_output.data_ptr(), value.data_ptr(),
                            sampling_locations.data_ptr(), attention_weights.data_ptr(), ptr(gv),
-                           ptr(gl), ptr(ga), ptr(ws), ws_len, _stream_ptr(stream))
+                           ptr(gl), ptr(ga), flags, ptr(ws), ws_len, _stream_ptr(stream))
     _raise_for(lib, st, "msda_backward")
     return gv, gl, ga
 

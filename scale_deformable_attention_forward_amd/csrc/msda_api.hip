@@ -17,16 +17,18 @@
 namespace msda {
 hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
                           const float* attn, void* out, hipStream_t stream);
-hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
-hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, const float* grad_out,
-                                const float* value, const float* loc, const float* attn, float* grad_value,
-                                float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream);
-hipError_t launch_backward_generic(const Geometry& g, int lpu, const float* grad_out, const float* value,
-                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
-                                   float* grad_attn, hipStream_t stream);
+hipError_t launch_zero_elems(void* p, int64_t n, int elem, hipStream_t stream);
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int bf16, int accumulate,
+                                const void* grad_out, const void* value, const float* loc, const float* attn,
+                                void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
+                                hipStream_t stream);
+hipError_t launch_backward_generic(const Geometry& g, int lpu, int bf16, int accumulate, const void* grad_out,
+                                   const void* value, const float* loc, const float* attn, void* grad_value,
+                                   float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream);
 struct AnchorWs;
 struct BandWs;
-size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws);
+size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws,
+                             float** partial);
 }  // namespace msda
 
 namespace {
@@ -150,11 +152,13 @@ int pick_vec(int64_t C_h, int elem, std::initializer_list<const void*> ptrs)
 // rounded up to a power of two (4 channels per lane).
 int fast_lanes(int64_t C_h) { return 1 << ilog2((int)((C_h + 3) / 4)); }
 
-// The fast backward path needs C_h % 4 == 0, C_h <= 64 and 16-byte aligned
-// channel rows; the tile pass packs pixel coordinates in 16 bits.
+// The fast backward path needs C_h % 4 == 0, C_h <= 64 (4 channels per lane,
+// at most 16 lanes per pixel), pixel coordinates that pack in 16 bits, and at
+// most 65535 (b, h) slabs (a grid dimension of the bucketing kernels).
 bool fast_backward_shape(const msda_problem& p)
 {
     if (p.C_h % 4 != 0 || p.C_h > 64) return false;
+    if (p.B * p.N_h > 65535) return false;
     for (int64_t l = 0; l < p.N_l; ++l)
         if (p.spatial_shapes[2 * l] > 60000 || p.spatial_shapes[2 * l + 1] > 60000) return false;
     return true;
@@ -165,17 +169,22 @@ bool fast_backward_shape(const msda_problem& p)
 // most kTileBins anchor bins, at most kMaxBandsPerLevel bands per level. A
 // band whose list is expected to hold more than two LDS passes of entries
 // (coarse levels, where many samples land on each pixel) is split into
-// chunks of its list, one workgroup each, finished with atomic adds.
+// chunks of its list, one workgroup each; each chunk writes a float32 partial
+// tile and the reduction pass adds a band's partial tiles in chunk order.
 // Returns false if a level cannot be tiled that way.
 bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
 {
     const int64_t pmax = (int64_t)(msda::kTileBlock / lpu) * msda::kTilePixelsPerGroup;
     const int64_t nsamp = p.N_q * p.N_p;
-    int64_t jobs = 0, bands = 0, cap = 0;
-    tp->any_chunked = 0;
+    const int64_t nwg = std::max<int64_t>(1, (nsamp + msda::kBandChunk - 1) / msda::kBandChunk);
+    if (nwg >= 65536) return false;  // grid x of the bucketing kernels stays small
+    int64_t jobs = 0, bands = 0, cap = 0, part = 0, pieces = 0;
     for (int64_t l = 0; l < msda::kMaxLevels; ++l) {
         tp->job_begin[l] = (int32_t)jobs;
         tp->band_begin[l] = (int32_t)bands;
+        tp->part_off[l] = (int32_t)part;
+        tp->rpiece_begin[l] = (int32_t)pieces;
+        tp->rpieces_per_band[l] = 1;
         if (l >= p.N_l) {
             tp->rows[l] = tp->row_bands[l] = tp->cols[l] = tp->col_bands[l] = tp->chunks[l] = 1;
             continue;
@@ -189,22 +198,34 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         // list entries of one band if locations spread evenly
         const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;
         int64_t chunks = (expect + 2 * msda::kTileEntries - 1) / (2 * msda::kTileEntries);
-        chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, 1024));
+        chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, std::min<int64_t>(nwg, 1024)));  // >= 1 run each
         tp->rows[l] = (int32_t)rows;
         tp->row_bands[l] = (int32_t)rb;
         tp->cols[l] = (int32_t)cols;
         tp->col_bands[l] = (int32_t)cb;
         tp->chunks[l] = (int32_t)chunks;
-        if (chunks > 1) tp->any_chunked = 1;
         jobs += rb * cb * chunks;
         bands += rb * cb;
         cap += nsamp * (cb > 1 ? 4 : 2);  // a sample touches at most 2 row bands x 2 column bands
+        if (chunks > 1) {
+            const int64_t tile = rows * cols * p.C_h;  // floats of one partial tile
+            part += rb * cb * chunks * tile;
+            const int64_t ppb = (tile / 4 + msda::kReduceF4 - 1) / msda::kReduceF4;
+            tp->rpieces_per_band[l] = (int32_t)ppb;
+            pieces += rb * cb * ppb;
+        }
+        if (part >= kIndexLimit || pieces >= kIndexLimit) return false;
     }
     tp->job_begin[msda::kMaxLevels] = (int32_t)jobs;
+    tp->rpiece_begin[msda::kMaxLevels] = (int32_t)pieces;
     tp->jobs = (int32_t)jobs;
     tp->bands = (int32_t)bands;
+    tp->rpieces = (int32_t)pieces;
+    tp->nwg = (int32_t)nwg;
     tp->cap = cap;
-    return jobs < kIndexLimit && cap < kIndexLimit;
+    tp->part_per_slab = part;
+    return jobs < kIndexLimit && cap < kIndexLimit && bands * nwg + 1 < kIndexLimit &&
+           (int64_t)p.B * p.N_h * (bands * nwg + 1) < kIndexLimit;
 }
 
 // Fast-path workspace bytes for `p` (0 if the tiled pass cannot take it).
@@ -212,7 +233,14 @@ size_t fast_workspace_bytes(const msda_problem& p, const Geometry& g)
 {
     TilePlan tp = {};
     if (!plan_tiles(p, fast_lanes(p.C_h), &tp)) return 0;
-    return msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr);
+    return msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr, nullptr);
+}
+
+// Generic-path workspace bytes: a float32 accumulator of value's shape for
+// bfloat16 grad_value, nothing for float32.
+size_t generic_workspace_bytes(const msda_problem& p, const Sizes& z)
+{
+    return p.value_dtype == MSDA_BF16 ? (size_t)z.value_elems * 4 : 0;
 }
 
 }  // namespace
@@ -259,31 +287,37 @@ msda_status msda_backward_workspace_size(const msda_problem* problem, size_t* by
     Sizes z;
     const msda_status st = check_problem(problem, &g, &z);
     if (st != MSDA_OK) return st;
-    if (problem->value_dtype != MSDA_F32) return MSDA_ERR_UNSUPPORTED;
-    *bytes = fast_backward_shape(*problem) ? fast_workspace_bytes(*problem, g) : 0;
+    // The path is chosen per call (it also depends on pointer alignment), so
+    // the size covers whichever of the two a call may take.
+    const size_t fast = fast_backward_shape(*problem) ? fast_workspace_bytes(*problem, g) : 0;
+    *bytes = std::max(fast, generic_workspace_bytes(*problem, z));
     return MSDA_OK;
 }
 
 msda_status msda_backward(const msda_problem* problem, const void* grad_output, const void* value,
                           const float* sampling_locations, const float* attention_weights, void* grad_value,
-                          float* grad_sampling_locations, float* grad_attention_weights, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream)
+                          float* grad_sampling_locations, float* grad_attention_weights, unsigned int flags,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     Geometry g;
     Sizes z;
     const msda_status st = check_problem(problem, &g, &z);
     if (st != MSDA_OK) return st;
+    if (flags & ~(unsigned int)MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) return MSDA_ERR_INVALID_ARGUMENT;
+    const int accumulate = (flags & MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) ? 1 : 0;
     if (!grad_value && !grad_sampling_locations && !grad_attention_weights) return MSDA_ERR_NOTHING_TO_COMPUTE;
-    if (problem->value_dtype != MSDA_F32) return MSDA_ERR_UNSUPPORTED;
     const bool empty = z.out_elems == 0;
+    const bool bf16 = problem->value_dtype == MSDA_BF16;
     if (!empty && (!grad_output || !value || !sampling_locations || !attention_weights))
         return MSDA_ERR_INVALID_ARGUMENT;
     const void* ins[4] = {grad_output, value, sampling_locations, attention_weights};
-    for (const void* p : ins)
-        if (p && !aligned(p, 4)) return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t in_align[4] = {(size_t)z.elem, (size_t)z.elem, 4, 4};
+    for (int i = 0; i < 4; ++i)
+        if (ins[i] && !aligned(ins[i], in_align[i])) return MSDA_ERR_INVALID_ARGUMENT;
     const void* outs[3] = {grad_value, grad_sampling_locations, grad_attention_weights};
-    for (const void* p : outs)
-        if (p && !aligned(p, 4)) return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t out_align[3] = {(size_t)z.elem, 4, 4};
+    for (int o = 0; o < 3; ++o)
+        if (outs[o] && !aligned(outs[o], out_align[o])) return MSDA_ERR_INVALID_ARGUMENT;
     const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
     const size_t in_bytes[4] = {z.out_bytes, z.value_bytes, loc_bytes, attn_bytes};
     const size_t out_bytes[3] = {z.value_bytes, loc_bytes, attn_bytes};
@@ -294,20 +328,26 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
             if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return MSDA_ERR_INVALID_ARGUMENT;
     }
 
-    // Fast path: 4 channels per lane and the destination-tiled grad_value
-    // pass (needs the workspace); otherwise one channel per lane and atomics.
+    // Fast path: 4 channels per lane (one 16-byte float32 or 8-byte bfloat16
+    // load) and the destination-tiled grad_value pass; otherwise one channel
+    // per lane and atomics.
     const int64_t C_h = problem->C_h;
+    const size_t row_align = 4 * (size_t)z.elem;
     TilePlan tp = {};
     const bool fast = fast_backward_shape(*problem) && plan_tiles(*problem, fast_lanes(C_h), &tp) &&
-                      aligned(value, 16) && aligned(grad_output, 16) && (!grad_value || aligned(grad_value, 16));
-    if (fast && grad_value && !empty) {
-        const size_t need = msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr);
-        if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
-        if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
-        for (int i = 0; i < 4; ++i)
-            if (overlap(workspace, need, ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
-        for (int o = 0; o < 3; ++o)
-            if (overlap(workspace, need, outs[o], out_bytes[o])) return MSDA_ERR_INVALID_ARGUMENT;
+                      aligned(value, row_align) && aligned(grad_output, row_align) &&
+                      (!grad_value || aligned(grad_value, row_align));
+    if (grad_value && !empty) {
+        const size_t need = fast ? msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr, nullptr)
+                                 : generic_workspace_bytes(*problem, z);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
+            if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
+            for (int i = 0; i < 4; ++i)
+                if (overlap(workspace, need, ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
+            for (int o = 0; o < 3; ++o)
+                if (overlap(workspace, need, outs[o], out_bytes[o])) return MSDA_ERR_INVALID_ARGUMENT;
+        }
     }
     const int lpu = fast ? fast_lanes(C_h) : 1 << ilog2((int)std::min<int64_t>(64, C_h));
     const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
@@ -320,21 +360,19 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
     if (fast && grad_value && !empty && (int64_t)tp.jobs * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
 
     hipError_t e = hipSuccess;
-    // grad_value is cleared unless the tile pass stores every element itself
-    const bool clear = grad_value && (empty || !fast || tp.any_chunked);
-    if (clear) e = msda::launch_zero(static_cast<float*>(grad_value), z.value_elems, stream);
-    if (e != hipSuccess) return MSDA_ERR_HIP;
-    if (empty) return MSDA_OK;
+    if (empty) {
+        // no query reaches grad_value: it is all zeros (or left as is)
+        if (grad_value && !accumulate) e = msda::launch_zero_elems(grad_value, z.value_elems, z.elem, stream);
+        return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+    }
     if (fast) {
-        e = msda::launch_backward_fast(g, tp, lpu, static_cast<const float*>(grad_output),
-                                       static_cast<const float*>(value), sampling_locations, attention_weights,
-                                       static_cast<float*>(grad_value), grad_sampling_locations,
+        e = msda::launch_backward_fast(g, tp, lpu, bf16, accumulate, grad_output, value, sampling_locations,
+                                       attention_weights, grad_value, grad_sampling_locations,
                                        grad_attention_weights, workspace, stream);
     } else {
-        e = msda::launch_backward_generic(g, lpu, static_cast<const float*>(grad_output),
-                                          static_cast<const float*>(value), sampling_locations, attention_weights,
-                                          static_cast<float*>(grad_value), grad_sampling_locations,
-                                          grad_attention_weights, stream);
+        e = msda::launch_backward_generic(g, lpu, bf16, accumulate, grad_output, value, sampling_locations,
+                                          attention_weights, grad_value, grad_sampling_locations,
+                                          grad_attention_weights, workspace, stream);
     }
     return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
 }

@@ -1,4 +1,5 @@
-// Backward of multi-scale deformable attention for gfx950 (float32).
+// Backward of multi-scale deformable attention for gfx950 (float32 or
+// bfloat16 storage, float32 arithmetic).
 //
 // For every (b, q, h) and sample (l, p), with G = grad_output[b, q, h*C_h:(h+1)*C_h]
 // and S the bilinear sample ("MS Deformable Attention Backward Kernel API
@@ -7,7 +8,7 @@
 //   grad_loc[b,q,h,l,p,x]  = A * <G, dS/dx> * dx/du_x    (same for y)
 //   grad_value[corner]    += A * w_corner * G             (every in-range corner)
 //
-// Fast path (C_h % 4 == 0, C_h <= 64, 16-byte aligned tensors), two kernels:
+// Fast path (C_h % 4 == 0, C_h <= 64, channel rows aligned to 4 elements):
 //  1. backward_fast_kernel, one unit = one (b, h, q) owned by C_h/4 lanes with
 //     4 channels per lane. Per chunk of up to SC samples the workgroup stages,
 //     one thread per (unit, sample), the corner pixel index, in-range mask,
@@ -16,21 +17,23 @@
 //     corners, form S, dS/dx and dS/dy, reduce the three dot products with
 //     DPP, and grad_A / grad_loc leave through LDS as coalesced stores. When
 //     grad_value is wanted, the staging also writes each sample's anchor
-//     corner (x0, y0) and fractions to the workspace.
-//  2. tile_scatter_kernel computes grad_value by destination instead of by
-//     source, so no float atomics sit on the hot path (global float atomics
-//     run at about one 128-byte line per request and LDS float atomics are an
-//     order of magnitude slower than LDS integer atomics on this part). Each
-//     level is cut into tiles of rows x cols pixels; a workgroup takes one
-//     tile (and, for dense coarse levels, one chunk of the level's samples),
-//     selects the samples whose 2x2 corner block touches the tile, bins them
-//     by anchor corner with LDS integer atomics, and then each destination
-//     pixel's lane group sums A * w * G over the four neighbouring anchor bins
-//     in registers (float64 within a pass). A tile written by one workgroup is stored; tiles split
-//     over several sample chunks are added with float atomics into a cleared
-//     grad_value (few: one per element per chunk).
+//     corner (x0, y0), fractions and weight to the workspace.
+//  2. grad_value by destination instead of by source, so no float atomics and
+//     no order-dependent sums (global float atomics run at about one 128-byte
+//     line per request and LDS float atomics are an order of magnitude slower
+//     than LDS integer atomics on this part). Each level is cut into bands of
+//     rows x cols pixels; band_count / band_scan / band_fill bucket the
+//     samples into one list per (b, h, band); tile_scatter_kernel takes one
+//     band (and, for dense coarse levels, one chunk of its list), sorts the
+//     entries by anchor corner in LDS, and each destination pixel's lane group
+//     sums A * w * G over its four neighbouring anchor bins in registers.
+//     A band of one chunk is stored directly; the chunks of a split band write
+//     float32 partial tiles to the workspace and band_reduce_kernel adds them
+//     in chunk order. grad_value is therefore bitwise reproducible.
 // Generic path (any C_h / alignment): backward_generic_kernel, one channel per
-// lane, grad_value through float atomics issued one channel per lane.
+// lane, grad_value through float atomics issued one channel per lane (into
+// grad_value for float32, into a float32 workspace then converted for
+// bfloat16); its grad_value may differ in the last bits from run to run.
 #include <algorithm>
 
 #include "msda_device.h"
@@ -59,6 +62,25 @@ __global__ __launch_bounds__(kBlock) void zero1_kernel(float* __restrict__ p, in
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+__global__ __launch_bounds__(kBlock) void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+// bfloat16 grad_value of the generic path from its float32 accumulator:
+// dst = RNE(acc (+ dst when accumulating)).
+__global__ __launch_bounds__(kBlock) void acc_to_bf16_kernel(const float* __restrict__ acc,
+                                                             uint16_t* __restrict__ dst, int64_t n,
+                                                             int accumulate)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float v = acc[i] + (accumulate ? bf16_to_f32(dst[i]) : 0.f);
+        dst[i] = f32_to_bf16_rne(v);
+    }
 }
 
 // Sum over aligned groups of LPU lanes; every lane of a group gets the total
@@ -229,12 +251,12 @@ __device__ __forceinline__ void store_results(const Geometry& g, const float4* s
 }
 
 // ---------------------------------------------------------------------------
-// Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, float4-aligned
-// tensors. LPU lanes per unit, 4 channels per lane.
-template <int LPU>
+// Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, channel rows
+// aligned to 4 elements. LPU lanes per unit, 4 channels per lane.
+template <typename T, int LPU>
 __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max,
-                                                               const float* __restrict__ grad_out,
-                                                               const float* __restrict__ value,
+                                                               const T* __restrict__ grad_out,
+                                                               const T* __restrict__ value,
                                                                const float* __restrict__ loc,
                                                                const float* __restrict__ attn,
                                                                float* __restrict__ grad_loc,
@@ -259,10 +281,10 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
     const int c0 = lig * VEC;
     const bool lane_ok = unit_ok && c0 < g.Ch;
-    const float* vslab = value + value_slab_offset(g, ui.b, ui.h) + c0;
+    const T* vslab = value + value_slab_offset(g, ui.b, ui.h) + c0;
     float G[VEC] = {0.f, 0.f, 0.f, 0.f};
     if (lane_ok && want_dots)
-        VecIO<float, VEC>::load(grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch + c0, G);
+        VecIO<T, VEC>::load(grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch + c0, G);
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
@@ -280,10 +302,10 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
                 float v00[VEC] = {0.f, 0.f, 0.f, 0.f}, v01[VEC] = {0.f, 0.f, 0.f, 0.f};
                 float v10[VEC] = {0.f, 0.f, 0.f, 0.f}, v11[VEC] = {0.f, 0.f, 0.f, 0.f};
                 if (lane_ok) {
-                    if (r.mask & 1) VecIO<float, VEC>::load(vslab + o00, v00);
-                    if (r.mask & 2) VecIO<float, VEC>::load(vslab + o00 + pstride, v01);
-                    if (r.mask & 4) VecIO<float, VEC>::load(vslab + o10, v10);
-                    if (r.mask & 8) VecIO<float, VEC>::load(vslab + o10 + pstride, v11);
+                    if (r.mask & 1) VecIO<T, VEC>::load(vslab + o00, v00);
+                    if (r.mask & 2) VecIO<T, VEC>::load(vslab + o00 + pstride, v01);
+                    if (r.mask & 4) VecIO<T, VEC>::load(vslab + o10, v10);
+                    if (r.mask & 8) VecIO<T, VEC>::load(vslab + o10 + pstride, v11);
                 }
                 float pa = 0.f, px = 0.f, py = 0.f;
 #pragma unroll
@@ -310,13 +332,13 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 // Fast path, grad_value by destination.
 //
 // Workspace views: per-sample arrays written by backward_fast_kernel, the
-// per-(slab, band) counts / cursors / offsets and the band lists (SoA, `cap`
+// per-(slab, band, run) counts and offsets and the band lists (SoA, `cap`
 // entries reserved per slab; entry = sample index k = q * N_p + p within its
-// (slab, level), anchor, fractions, attention weight).
+// (slab, level), anchor, fractions, attention weight). Run w of a band holds
+// that band's samples among k in [w * kBandChunk, (w + 1) * kBandChunk).
 struct BandWs {
-    int* cnt;       // [slabs][bands]
-    int* cursor;    // [slabs][bands]
-    int* off;       // [slabs][bands + 1]
+    int* cnt;       // [slabs][bands][nwg]
+    int* off;       // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
     uint32_t* k;
     uint32_t* anchor;
     float* fx;
@@ -325,13 +347,13 @@ struct BandWs {
 };
 
 struct LevelTiles {
-    int H, W, start, R, CW, nbr, nbc, nch, band0, job0;
+    int H, W, start, R, CW, nbr, nbc, nch, band0, job0, part;
 };
 
 // Tile geometry of level l (static indices only, so the plan stays in kernel-argument memory).
 __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TilePlan& tp, int l)
 {
-    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0};
+    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kMaxLevels; ++k) {
         if (k == l) {
@@ -345,6 +367,7 @@ __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TileP
             t.nch = tp.chunks[k];
             t.band0 = tp.band_begin[k];
             t.job0 = tp.job_begin[k];
+            t.part = tp.part_off[k];
         }
     }
     return t;
@@ -377,17 +400,19 @@ __device__ __forceinline__ void unpack_anchor(uint32_t a, int& x0, int& y0)
     y0 = (int)(a >> 16) - 2;
 }
 
-// Bucketing 1/3: per-(slab, band) sample counts. Grid (sample chunk, level, slab).
+// Bucketing 1/3: per-(slab, band, run) sample counts. Grid (run, level,
+// slab); every workgroup writes the counts of all bands of its level, so the
+// array needs no clearing.
 __global__ __launch_bounds__(kBandBlock) void band_count_kernel(Geometry g, TilePlan tp,
                                                                 const uint32_t* __restrict__ anchor,
                                                                 int* __restrict__ cnt)
 {
     __shared__ int hist[kMaxBandsPerLevel];
-    const int l = blockIdx.y, slab = blockIdx.z;
+    const int wg = blockIdx.x, l = blockIdx.y, slab = blockIdx.z;
     const LevelTiles t = level_tiles(g, tp, l);
     const int nb = t.nbr * t.nbc;
     const int nsamp = g.Nq * g.Np;
-    const int k0 = blockIdx.x * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
+    const int k0 = wg * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
     for (int i = threadIdx.x; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
     const uint32_t* an = anchor + (size_t)(slab * g.Nl + l) * nsamp;
@@ -398,19 +423,19 @@ __global__ __launch_bounds__(kBandBlock) void band_count_kernel(Geometry g, Tile
         for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += kBandBlock)
-        if (hist[i]) atomicAdd(&cnt[slab * tp.bands + t.band0 + i], hist[i]);
+    int* c = cnt + ((size_t)slab * tp.bands + t.band0) * tp.nwg + wg;
+    for (int i = threadIdx.x; i < nb; i += kBandBlock) c[(size_t)i * tp.nwg] = hist[i];
 }
 
-// Bucketing 2/3: exclusive prefix of the band counts of each slab.
+// Bucketing 2/3: exclusive prefix of the (band, run) counts of each slab.
 __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const int* __restrict__ cnt,
                                                            int* __restrict__ off)
 {
     __shared__ int s_wave[kBlock / kWave];
-    const int slab = blockIdx.x, n = tp.bands;
+    const int slab = blockIdx.x, n = tp.bands * tp.nwg;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int* c = cnt + slab * n;
-    int* o = off + slab * (n + 1);
+    const int* c = cnt + (size_t)slab * n;
+    int* o = off + (size_t)slab * (n + 1);
     int carry = 0;
     for (int base = 0; base < n; base += kBlock) {
         const int i = base + tid;
@@ -436,9 +461,10 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
 }
 
 // Bucketing 3/3: fill the band lists. Grid as band_count_kernel. Each
-// workgroup orders its entries by band in LDS, reserves one contiguous run
-// per band it touches, and writes every run with consecutive stores.
-// Dynamic LDS: 3 * (max_bands + 1) ints, then max_entries (k, band) pairs
+// workgroup orders its entries by band in LDS and writes its run of every
+// band at the offset the scan gave it, with consecutive stores. (Order inside
+// a run is arbitrary; the tile pass orders what it sums.)
+// Dynamic LDS: 2 * (max_bands + 1) ints, then max_entries (k, band) pairs
 // (kBandChunk samples times the most bands one sample can touch).
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
                                                                const uint32_t* __restrict__ anchor,
@@ -450,17 +476,16 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     constexpr int kWaves = kBandBlock / kWave;
     extern __shared__ int dyn[];
     int* hist = dyn;
-    int* base = hist + max_bands + 1;
-    int* loff = base + max_bands + 1;
+    int* loff = hist + max_bands + 1;
     uint32_t* s_k = reinterpret_cast<uint32_t*>(loff + max_bands + 1);
     uint16_t* s_band = reinterpret_cast<uint16_t*>(s_k + max_entries);
     __shared__ int s_wave[kWaves];
     const int tid = threadIdx.x;
-    const int l = blockIdx.y, slab = blockIdx.z;
+    const int wg = blockIdx.x, l = blockIdx.y, slab = blockIdx.z;
     const LevelTiles t = level_tiles(g, tp, l);
     const int nb = t.nbr * t.nbc;
     const int nsamp = g.Nq * g.Np;
-    const int k0 = blockIdx.x * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
+    const int k0 = wg * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
     for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
     const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
@@ -495,13 +520,7 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
         __syncthreads();
     }
     if (tid == 0) loff[nb] = carry;
-    for (int i = tid; i < nb; i += kBandBlock) {
-        if (hist[i]) {
-            const int sb = slab * tp.bands + t.band0 + i;
-            base[i] = w.off[slab * (tp.bands + 1) + t.band0 + i] + atomicAdd(&w.cursor[sb], hist[i]);
-            hist[i] = 0;
-        }
-    }
+    for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
     for (int k = k0 + tid; k < k1; k += kBandBlock) {
         int x0, y0, bands[4];
@@ -516,9 +535,10 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     __syncthreads();
     const int total = loff[nb];
     const size_t lbase = (size_t)slab * tp.cap;
+    const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)t.band0 * tp.nwg + wg;
     for (int i = tid; i < total; i += kBandBlock) {
         const int bnd = s_band[i];
-        const size_t pos = lbase + base[bnd] + (i - loff[bnd]);
+        const size_t pos = lbase + run_off[(size_t)bnd * tp.nwg] + (i - loff[bnd]);
         const uint32_t k = s_k[i];
         w.k[pos] = k;
         w.anchor[pos] = anchor[sbase + k];
@@ -531,24 +551,55 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
 // Dynamic LDS bytes of band_fill_kernel.
 static size_t band_fill_lds(int max_bands, int max_entries)
 {
-    return (size_t)3 * (max_bands + 1) * sizeof(int) + (size_t)max_entries * (sizeof(uint32_t) + sizeof(uint16_t));
+    return (size_t)2 * (max_bands + 1) * sizeof(int) + (size_t)max_entries * (sizeof(uint32_t) + sizeof(uint16_t));
+}
+
+// Band of level-local index `band`: rows [r0, r0 + th), columns [c0, c0 + tw).
+struct BandRect {
+    int r0, c0, th, tw;
+};
+__device__ __forceinline__ BandRect band_rect(const LevelTiles& t, int band)
+{
+    const int kr = band / t.nbc, kc = band - kr * t.nbc;
+    BandRect r;
+    r.r0 = kr * t.R;
+    r.c0 = kc * t.CW;
+    r.th = min(t.H, r.r0 + t.R) - r.r0;
+    r.tw = min(t.W, r.c0 + t.CW) - r.c0;
+    return r;
+}
+
+// Final grad_value store of 4 channels: dst = v (+ dst when accumulating).
+template <typename T>
+__device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
+{
+    float v[4] = {a.x, a.y, a.z, a.w};
+    if (accumulate) {
+        float o[4];
+        VecIO<T, 4>::load(dst, o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += o[i];
+    }
+    VecIO<T, 4>::store(dst, v);
 }
 
 // Tile kernel. LPU lanes per destination pixel (4 channels per lane),
 // kTileBlock / LPU pixel groups per workgroup, each owning up to
 // kTilePixelsPerGroup pixels of the tile.
-template <int LPU>
-__global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(Geometry g, TilePlan tp, BandWs w,
-                                                                  const float* __restrict__ grad_out,
-                                                                  float* __restrict__ grad_value)
+template <typename T, int LPU>
+__global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
+    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
+    float* __restrict__ partial, int accumulate)
 {
     constexpr int NG = kTileBlock / LPU;
     constexpr int PPG = kTilePixelsPerGroup;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
     __shared__ float4 s_ent[E];              // (fx, fy, A, q)
+    __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
     __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
-    __shared__ uint16_t s_sorted[E];         // staged entries ordered by bin
+    __shared__ uint16_t s_binned[E];         // staged entries grouped by bin (any order inside)
+    __shared__ uint16_t s_sorted[E];         // staged entries ordered by (bin, k)
     __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_sorted
     __shared__ int s_cursor[kTileBins];
     __shared__ int s_wave[kWaves];
@@ -566,30 +617,36 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const LevelTiles t = level_tiles(g, tp, l);
     const int local = job - t.job0;
     const int band = local / t.nch, chunk = local - band * t.nch;
-    const int kr = band / t.nbc, kc = band - kr * t.nbc;
-    const int r0 = kr * t.R, r1 = min(t.H, r0 + t.R);
-    const int c0 = kc * t.CW, c1 = min(t.W, c0 + t.CW);
-    const int tw = c1 - c0, th = r1 - r0, P = tw * th;
+    const BandRect br = band_rect(t, band);
+    const int r0 = br.r0, c0 = br.c0, tw = br.tw, P = br.tw * br.th;
     const int nbw = tw + 1;                  // anchor bins cover rows r0-1..r1-1, cols c0-1..c1-1
-    const int nbins = (th + 1) * nbw;
-    const int sb = slab * tp.bands + t.band0 + band;
-    const int n = w.cnt[sb], o = w.off[slab * (tp.bands + 1) + t.band0 + band];
-    const int e_begin = o + (int)((int64_t)n * chunk / t.nch), e_end = o + (int)((int64_t)n * (chunk + 1) / t.nch);
+    const int nbins = (br.th + 1) * nbw;
+    // this chunk's runs [w_lo, w_hi) of the band's list; run_off[w] is where run w starts
+    const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
+    const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
     const size_t lbase = (size_t)slab * tp.cap;
-    const float* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
+    const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
     const bool lane_ok = ch < g.Ch;
-    const float* gl = grow0 + ch;
+    const T* gl = grow0 + ch;
 
     float4 acc[PPG];
 #pragma unroll
     for (int m = 0; m < PPG; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    for (int p0 = e_begin; p0 < e_end; p0 += E) {
-        const int m_cnt = min(E, e_end - p0);
+    // A pass stages whole runs (at most E entries; one run never exceeds
+    // kBandChunk <= E), so which entries share a pass does not depend on the
+    // order inside runs; inside a pass every bin is summed in k order. The
+    // sums are therefore the same on every call.
+    for (int wr = w_lo; wr < w_hi;) {
+        const int p0 = run_off[wr];
+        int wn = wr + 1;
+        while (wn < w_hi && run_off[wn + 1] - p0 <= E) ++wn;
+        const int m_cnt = run_off[wn] - p0;
+        wr = wn;
         // stage a pass of list entries and count them per anchor bin
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
@@ -598,8 +655,10 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             int x0, y0;
             unpack_anchor(w.anchor[pos], x0, y0);
             const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            const int q = (int)w.k[pos] / g.Np;
+            const uint32_t k = w.k[pos];
+            const int q = (int)k / g.Np;
             s_ent[i] = make_float4(w.fx[pos], w.fy[pos], w.a[pos], __int_as_float(q));
+            s_key[i] = k;
             s_bin_of[i] = (uint16_t)bin;
             atomicAdd(&s_cursor[bin], 1);
         }
@@ -629,7 +688,17 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         }
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
         __syncthreads();
-        for (int i = tid; i < m_cnt; i += kTileBlock) s_sorted[atomicAdd(&s_cursor[s_bin_of[i]], 1)] = (uint16_t)i;
+        for (int i = tid; i < m_cnt; i += kTileBlock) s_binned[atomicAdd(&s_cursor[s_bin_of[i]], 1)] = (uint16_t)i;
+        __syncthreads();
+        // rank every entry among its bin by k (keys are unique within a band list)
+        for (int i = tid; i < m_cnt; i += kTileBlock) {
+            const int bin = s_bin_of[i];
+            const uint32_t key = s_key[i];
+            const int b0 = s_bstart[bin], b1 = s_bstart[bin + 1];
+            int rank = 0;
+            for (int j = b0; j < b1; ++j) rank += s_key[s_binned[j]] < key ? 1 : 0;
+            s_sorted[b0 + rank] = (uint16_t)i;
+        }
         __syncthreads();
         // every pixel group sums its pixels' four neighbouring bins; partial sums
         // per bin keep float32 rounding chains short
@@ -647,25 +716,28 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                     const int e1 = s_bstart[bin + 1];
                     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
                     for (int e = s_bstart[bin]; e < e1; e += 4) {
-                        float4 ent[4], gv[4];
+                        float4 ent[4];
+                        float gv[4][4];
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             ent[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                            gv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                            float t4[4] = {0.f, 0.f, 0.f, 0.f};
                             if (e + u < e1) {
                                 ent[u] = s_ent[s_sorted[e + u]];
-                                gv[u] = *reinterpret_cast<const float4*>(gl + __float_as_int(ent[u].w) * gq);
+                                VecIO<T, 4>::load(gl + __float_as_int(ent[u].w) * gq, t4);
                             }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) gv[u][i] = t4[i];
                         }
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             const float wx = dx ? ent[u].x : 1.f - ent[u].x;
                             const float wy = dy ? ent[u].y : 1.f - ent[u].y;
                             const float coef = ent[u].z * (wx * wy);
-                            sum.x = __builtin_fmaf(coef, gv[u].x, sum.x);
-                            sum.y = __builtin_fmaf(coef, gv[u].y, sum.y);
-                            sum.z = __builtin_fmaf(coef, gv[u].z, sum.z);
-                            sum.w = __builtin_fmaf(coef, gv[u].w, sum.w);
+                            sum.x = __builtin_fmaf(coef, gv[u][0], sum.x);
+                            sum.y = __builtin_fmaf(coef, gv[u][1], sum.y);
+                            sum.z = __builtin_fmaf(coef, gv[u][2], sum.z);
+                            sum.w = __builtin_fmaf(coef, gv[u][3], sum.w);
                         }
                     }
                     pix.x += sum.x;
@@ -682,56 +754,85 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         __syncthreads();
     }
 
-    // Write the tile: one workgroup per band stores; bands split over several
-    // chunks are added into the cleared grad_value, one channel per lane
-    // through LDS so that every atomic instruction covers whole channel rows.
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    float* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
+    if (!lane_ok) return;
     if (t.nch == 1) {
-        if (!lane_ok) return;
+        // the band's only job: store the final values
+        const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+        T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
 #pragma unroll
         for (int m = 0; m < PPG; ++m) {
             const int p = grp + m * NG;
             if (p >= P) break;
             const int py = p / tw, px = p - py * tw;
-            *reinterpret_cast<float4*>(out + ((r0 + py) * t.W + c0 + px) * pstride + ch) = acc[m];
+            store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[m], accumulate);
         }
         return;
     }
-    float* stage = reinterpret_cast<float*>(s_ent);  // E float4 of staging
-    const int ppr = (E * 4) / g.Ch;                  // pixels per staging round
-    for (int q0 = 0; q0 < P; q0 += ppr) {
-        const int q1 = min(P, q0 + ppr);
-        if (lane_ok) {
+    // one chunk of a split band: its partial tile, pixel-major, C_h floats per pixel
+    float* slot = partial + (size_t)slab * tp.part_per_slab + t.part +
+                  (size_t)(band * t.nch + chunk) * (t.R * t.CW) * g.Ch;
 #pragma unroll
-            for (int m = 0; m < PPG; ++m) {
-                const int p = grp + m * NG;
-                if (p >= q0 && p < q1) *reinterpret_cast<float4*>(stage + (p - q0) * g.Ch + ch) = acc[m];
-            }
+    for (int m = 0; m < PPG; ++m) {
+        const int p = grp + m * NG;
+        if (p >= P) break;
+        *reinterpret_cast<float4*>(slot + p * g.Ch + ch) = acc[m];
+    }
+}
+
+// Adds the partial tiles of split bands in chunk order and stores grad_value.
+// Grid: (reduction piece, slab); a piece is up to kReduceF4 float4s of one band.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void band_reduce_kernel(Geometry g, TilePlan tp,
+                                                             const float* __restrict__ partial,
+                                                             T* __restrict__ grad_value, int accumulate)
+{
+    const int piece = blockIdx.x, slab = blockIdx.y;
+    const int b = slab / g.Nh, h = slab - b * g.Nh;
+    int l = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k)
+        if (piece >= tp.rpiece_begin[k] && piece < tp.rpiece_begin[k + 1]) l = k;
+    const LevelTiles t = level_tiles(g, tp, l);
+    int ppb = 1;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k)
+        if (k == l) ppb = tp.rpieces_per_band[k];
+    const int local = piece - tp.rpiece_begin[l];
+    const int band = local / ppb, sub = local - band * ppb;
+    const BandRect br = band_rect(t, band);
+    const int n4 = br.th * br.tw * g.Ch / 4;
+    const int i0 = sub * kReduceF4, i1 = min(n4, i0 + kReduceF4);
+    const size_t tile = (size_t)t.R * t.CW * g.Ch;
+    const float* slot0 = partial + (size_t)slab * tp.part_per_slab + t.part + (size_t)band * t.nch * tile;
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
+    for (int i = i0 + (int)threadIdx.x; i < i1; i += kBlock) {
+        float4 s = reinterpret_cast<const float4*>(slot0)[i];
+        for (int c = 1; c < t.nch; ++c) {
+            const float4 v = reinterpret_cast<const float4*>(slot0 + c * tile)[i];
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
         }
-        __syncthreads();
-        for (int i = tid; i < (q1 - q0) * g.Ch; i += kTileBlock) {
-            const float v = stage[i];
-            if (v != 0.f) {
-                const int pp = q0 + i / g.Ch, c = i - (i / g.Ch) * g.Ch;
-                const int yy = pp / tw, xx = pp - yy * tw;
-                unsafeAtomicAdd(out + ((r0 + yy) * t.W + c0 + xx) * pstride + c, v);
-            }
-        }
-        __syncthreads();
+        const int e = 4 * i;
+        const int p = e / g.Ch, ch = e - p * g.Ch;
+        const int py = p / br.tw, px = p - py * br.tw;
+        store_grad4(out + ((br.r0 + py) * t.W + br.c0 + px) * pstride + ch, s, accumulate);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Generic path: any C_h, any alignment. One channel per lane (LPU lanes per
-// unit, channels beyond LPU in a loop); grad_value via float atomics.
-template <int LPU>
+// unit, channels beyond LPU in a loop); grad_value via float atomics into
+// `gacc` (grad_value itself for float32, a float32 workspace for bfloat16).
+template <typename T, int LPU>
 __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, int sc_max,
-                                                                  const float* __restrict__ grad_out,
-                                                                  const float* __restrict__ value,
+                                                                  const T* __restrict__ grad_out,
+                                                                  const T* __restrict__ value,
                                                                   const float* __restrict__ loc,
                                                                   const float* __restrict__ attn,
-                                                                  float* __restrict__ grad_value,
+                                                                  float* __restrict__ gacc,
                                                                   float* __restrict__ grad_loc,
                                                                   float* __restrict__ grad_attn)
 {
@@ -751,9 +852,9 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     const int slab_off = value_slab_offset(g, ui.b, ui.h);
-    const float* vslab = value + slab_off;
-    float* gslab = grad_value ? grad_value + slab_off : nullptr;
-    const float* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
+    const T* vslab = value + slab_off;
+    float* gslab = gacc ? gacc + slab_off : nullptr;
+    const T* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
     const AnchorWs no_ws = {nullptr, nullptr, nullptr, nullptr};
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
@@ -772,12 +873,12 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
                 const int o11 = o10 + pstride;
                 float pa = 0.f, px = 0.f, py = 0.f;
                 for (int c = lig; c < g.Ch; c += LPU) {
-                    const float Gc = grow[c];
+                    const float Gc = load_f32(grow + c);
                     if (want_dots) {
-                        const float v00 = (r.mask & 1) ? vslab[o00 + c] : 0.f;
-                        const float v01 = (r.mask & 2) ? vslab[o01 + c] : 0.f;
-                        const float v10 = (r.mask & 4) ? vslab[o10 + c] : 0.f;
-                        const float v11 = (r.mask & 8) ? vslab[o11 + c] : 0.f;
+                        const float v00 = (r.mask & 1) ? load_f32(vslab + o00 + c) : 0.f;
+                        const float v01 = (r.mask & 2) ? load_f32(vslab + o01 + c) : 0.f;
+                        const float v10 = (r.mask & 4) ? load_f32(vslab + o10 + c) : 0.f;
+                        const float v11 = (r.mask & 8) ? load_f32(vslab + o11 + c) : 0.f;
                         const float smp = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
                         const float dx = gyw * (v01 - v00) + r.fy * (v11 - v10);
                         const float dy = gxw * (v10 - v00) + r.fx * (v11 - v01);
@@ -810,20 +911,28 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
 // ---------------------------------------------------------------------------
 // host launchers
 
+static unsigned grid_for(int64_t n)
+{
+    return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + kBlock - 1) / kBlock, 8192));
+}
+
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
     const int64_t n4 = ((uintptr_t)p % 16 == 0) ? n / 4 : 0;
     const int64_t rest = n - 4 * n4;
-    if (n4 > 0) {
-        const int64_t blocks = std::min<int64_t>((n4 + kBlock - 1) / kBlock, 8192);
-        hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                           reinterpret_cast<float4*>(p), n4);
-    }
-    if (rest > 0) {
-        const int64_t blocks = std::min<int64_t>((rest + kBlock - 1) / kBlock, 8192);
-        hipLaunchKernelGGL(zero1_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, p + 4 * n4, rest);
-    }
+    if (n4 > 0)
+        hipLaunchKernelGGL(zero4_kernel, dim3(grid_for(n4)), dim3(kBlock), 0, stream, reinterpret_cast<float4*>(p), n4);
+    if (rest > 0) hipLaunchKernelGGL(zero1_kernel, dim3(grid_for(rest)), dim3(kBlock), 0, stream, p + 4 * n4, rest);
+    return hipGetLastError();
+}
+
+// Clear n elements of grad_value in its storage type (4 or 2 bytes).
+hipError_t launch_zero_elems(void* p, int64_t n, int elem, hipStream_t stream)
+{
+    if (elem == 4) return launch_zero(static_cast<float*>(p), n, stream);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_u16_kernel, dim3(grid_for(n)), dim3(kBlock), 0, stream, static_cast<uint16_t*>(p), n);
     return hipGetLastError();
 }
 
@@ -835,48 +944,55 @@ static int samples_per_chunk(int S, int upb)
     return sc;
 }
 
-template <int LPU>
-static hipError_t launch_fast_t(const Geometry& g, const float* grad_out, const float* value, const float* loc,
+template <typename T, int LPU>
+static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const void* value, const float* loc,
                                 const float* attn, float* grad_loc, float* grad_attn, AnchorWs ws,
                                 hipStream_t stream)
 {
     constexpr int upb = kBlock / LPU;
     const int sc = samples_per_chunk(g.S, upb);
     const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
-    hipLaunchKernelGGL((backward_fast_kernel<LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc, grad_out,
-                       value, loc, attn, grad_loc, grad_attn, ws);
+    hipLaunchKernelGGL((backward_fast_kernel<T, LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                       static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn, grad_loc,
+                       grad_attn, ws);
     return hipGetLastError();
 }
 
-template <int LPU>
-static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const float* grad_out,
-                                 float* grad_value, hipStream_t stream)
+template <typename T, int LPU>
+static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
+                                 void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
-    hipLaunchKernelGGL((tile_scatter_kernel<LPU>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g, tp, w,
-                       grad_out, grad_value);
+    hipLaunchKernelGGL((tile_scatter_kernel<T, LPU>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g, tp,
+                       w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
+    if (tp.rpieces > 0)
+        hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
+                           0, stream, g, tp, partial, static_cast<T*>(grad_value), accumulate);
     return hipGetLastError();
 }
 
-template <int LPU>
-static hipError_t launch_generic_t(const Geometry& g, const float* grad_out, const float* value,
-                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
-                                   float* grad_attn, hipStream_t stream)
+template <typename T, int LPU>
+static hipError_t launch_generic_t(const Geometry& g, const void* grad_out, const void* value, const float* loc,
+                                   const float* attn, float* gacc, float* grad_loc, float* grad_attn,
+                                   hipStream_t stream)
 {
     constexpr int upb = kBlock / LPU;
     const int sc = samples_per_chunk(g.S, upb);
     const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
-    hipLaunchKernelGGL((backward_generic_kernel<LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                       grad_out, value, loc, attn, grad_value, grad_loc, grad_attn);
+    hipLaunchKernelGGL((backward_generic_kernel<T, LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                       static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn, gacc, grad_loc,
+                       grad_attn);
     return hipGetLastError();
 }
 
 // Workspace of the fast path with grad_value: per-sample arrays (16 bytes per
-// sample), band counts / cursors / offsets, and the band lists (20 bytes per
-// reserved entry). Every piece starts 256-byte aligned.
+// sample), per-(band, run) counts and offsets, the band lists (20 bytes per
+// reserved entry) and the float32 partial tiles of split bands. Every piece
+// starts 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws)
+size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws,
+                             float** partial)
 {
     const size_t ns = (size_t)g.B * g.Nh * g.Nq * g.S;
     const size_t slabs = (size_t)g.B * g.Nh;
@@ -895,42 +1011,67 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     a.fy = reinterpret_cast<float*>(take(ns * 4));
     a.a = reinterpret_cast<float*>(take(ns * 4));
     BandWs w;
-    w.cnt = reinterpret_cast<int*>(take(slabs * nb * 4 * 2));  // counts, then cursors
-    w.cursor = w.cnt ? w.cnt + slabs * nb : nullptr;
-    w.off = reinterpret_cast<int*>(take(slabs * (nb + 1) * 4));
+    const size_t runs = nb * (size_t)tp.nwg;
+    w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
+    w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
     w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
     w.anchor = reinterpret_cast<uint32_t*>(take(cap * 4));
     w.fx = reinterpret_cast<float*>(take(cap * 4));
     w.fy = reinterpret_cast<float*>(take(cap * 4));
     w.a = reinterpret_cast<float*>(take(cap * 4));
+    float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
     if (bws) *bws = w;
+    if (partial) *partial = part;
     return at;
 }
 
-// Fast path. grad_value (if any) must already be cleared when tp.any_chunked.
-hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, const float* grad_out,
-                                const float* value, const float* loc, const float* attn, float* grad_value,
-                                float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream)
+template <typename T>
+static hipError_t launch_fast_typed(const Geometry& g, int lpu, const void* grad_out, const void* value,
+                                    const float* loc, const float* attn, float* grad_loc, float* grad_attn,
+                                    AnchorWs ws, hipStream_t stream)
+{
+    switch (lpu) {
+    case 1: return launch_fast_t<T, 1>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 2: return launch_fast_t<T, 2>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 4: return launch_fast_t<T, 4>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 8: return launch_fast_t<T, 8>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 16: return launch_fast_t<T, 16>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+static hipError_t launch_tiles_typed(const Geometry& g, const TilePlan& tp, int lpu, BandWs w, const void* grad_out,
+                                     void* grad_value, float* partial, int accumulate, hipStream_t stream)
+{
+    switch (lpu) {
+    case 1: return launch_tiles_t<T, 1>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 2: return launch_tiles_t<T, 2>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 4: return launch_tiles_t<T, 4>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 8: return launch_tiles_t<T, 8>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 16: return launch_tiles_t<T, 16>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Fast path. Every grad_value element is written by exactly one store (no
+// clearing needed); with `accumulate` the store adds the element's old value.
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int bf16, int accumulate,
+                                const void* grad_out, const void* value, const float* loc, const float* attn,
+                                void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
+                                hipStream_t stream)
 {
     AnchorWs ws = {nullptr, nullptr, nullptr, nullptr};
     BandWs bw = {};
-    if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw);
-    hipError_t e;
-    switch (lpu) {
-    case 1: e = launch_fast_t<1>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
-    case 2: e = launch_fast_t<2>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
-    case 4: e = launch_fast_t<4>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
-    case 8: e = launch_fast_t<8>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
-    case 16: e = launch_fast_t<16>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream); break;
-    default: return hipErrorInvalidValue;
-    }
+    float* partial = nullptr;
+    if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw, &partial);
+    hipError_t e = bf16 ? launch_fast_typed<uint16_t>(g, lpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream)
+                        : launch_fast_typed<float>(g, lpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
     if (e != hipSuccess || !grad_value) return e;
     const int slabs = g.B * g.Nh;
-    // bucket the samples by band
-    e = launch_zero(reinterpret_cast<float*>(bw.cnt), (int64_t)slabs * tp.bands * 2, stream);
-    if (e != hipSuccess) return e;
-    const dim3 bgrid((g.Nq * g.Np + kBandChunk - 1) / kBandChunk, g.Nl, slabs);
+    // bucket the samples by band, one run per (band, bucketing workgroup)
+    const dim3 bgrid(tp.nwg, g.Nl, slabs);
     hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
     hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
     int max_bands = 1, max_mult = 2;
@@ -949,31 +1090,48 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                        ws.fy, ws.a, max_bands, max_entries);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
+                : launch_tiles_typed<float>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream);
+}
+
+template <typename T>
+static hipError_t launch_generic_typed(const Geometry& g, int lpu, const void* grad_out, const void* value,
+                                       const float* loc, const float* attn, float* gacc, float* grad_loc,
+                                       float* grad_attn, hipStream_t stream)
+{
     switch (lpu) {
-    case 1: return launch_tiles_t<1>(g, tp, bw, grad_out, grad_value, stream);
-    case 2: return launch_tiles_t<2>(g, tp, bw, grad_out, grad_value, stream);
-    case 4: return launch_tiles_t<4>(g, tp, bw, grad_out, grad_value, stream);
-    case 8: return launch_tiles_t<8>(g, tp, bw, grad_out, grad_value, stream);
-    case 16: return launch_tiles_t<16>(g, tp, bw, grad_out, grad_value, stream);
+    case 1: return launch_generic_t<T, 1>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 2: return launch_generic_t<T, 2>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 4: return launch_generic_t<T, 4>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 8: return launch_generic_t<T, 8>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 16: return launch_generic_t<T, 16>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 32: return launch_generic_t<T, 32>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    case 64: return launch_generic_t<T, 64>(g, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-// Generic path. grad_value (if any) must already be cleared.
-hipError_t launch_backward_generic(const Geometry& g, int lpu, const float* grad_out, const float* value,
-                                   const float* loc, const float* attn, float* grad_value, float* grad_loc,
-                                   float* grad_attn, hipStream_t stream)
+// Generic path. float32: atomics straight into grad_value (cleared first
+// unless accumulating). bfloat16: atomics into the float32 workspace
+// (value-sized, cleared here), then one RNE conversion into grad_value.
+hipError_t launch_backward_generic(const Geometry& g, int lpu, int bf16, int accumulate, const void* grad_out,
+                                   const void* value, const float* loc, const float* attn, void* grad_value,
+                                   float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream)
 {
-    switch (lpu) {
-    case 1: return launch_generic_t<1>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 2: return launch_generic_t<2>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 4: return launch_generic_t<4>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 8: return launch_generic_t<8>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 16: return launch_generic_t<16>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 32: return launch_generic_t<32>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    case 64: return launch_generic_t<64>(g, grad_out, value, loc, attn, grad_value, grad_loc, grad_attn, stream);
-    default: return hipErrorInvalidValue;
+    const int64_t nv = (int64_t)g.B * g.L * g.Nh * g.Ch;
+    float* gacc = nullptr;
+    hipError_t e = hipSuccess;
+    if (grad_value) {
+        gacc = bf16 ? static_cast<float*>(workspace) : static_cast<float*>(grad_value);
+        if (bf16 || !accumulate) e = launch_zero(gacc, nv, stream);
+        if (e != hipSuccess) return e;
     }
+    e = bf16 ? launch_generic_typed<uint16_t>(g, lpu, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream)
+             : launch_generic_typed<float>(g, lpu, grad_out, value, loc, attn, gacc, grad_loc, grad_attn, stream);
+    if (e != hipSuccess || !grad_value || !bf16) return e;
+    hipLaunchKernelGGL(acc_to_bf16_kernel, dim3(grid_for(nv)), dim3(kBlock), 0, stream, gacc,
+                       static_cast<uint16_t*>(grad_value), nv, accumulate);
+    return hipGetLastError();
 }
 
 }  // namespace msda

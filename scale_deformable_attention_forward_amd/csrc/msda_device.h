@@ -39,8 +39,12 @@ struct Geometry {
 
 // Destination-tiled grad_value pass (backward). Every level is cut into
 // bands (tiles) of `rows` x `cols` pixels. Samples are bucketed by the bands
-// their 2x2 corner block touches into one contiguous list per (b, h, band);
-// a tile job is (band, chunk of that band's list).
+// their 2x2 corner block touches into one list per (b, h, band), made of one
+// run per bucketing workgroup (kBandChunk consecutive samples) in workgroup
+// order. A tile job is (band, chunk), a chunk being a range of runs. A band
+// of one chunk is stored by its job; the jobs of a band split into several
+// chunks write float32 partial tiles, which a reduction pass adds in chunk
+// order.
 constexpr int kTileBlock = 512;          // threads per tile workgroup
 constexpr int kTilePixelsPerGroup = 8;   // destination pixels owned by one lane group
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
@@ -48,12 +52,16 @@ constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (
 constexpr int kBandBlock = 256;          // threads of the bucketing kernels
 constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
+constexpr int kReduceF4 = 1024;          // float4s of a band one reduction workgroup adds up
+static_assert(kBandChunk <= kTileEntries, "one run (<= kBandChunk entries) must fit one LDS pass");
 
 struct TilePlan {
     int32_t jobs;                        // tile jobs per (b, h) slab
     int32_t bands;                       // bands per slab
-    int32_t any_chunked;                 // some band is split over chunks (atomic flush)
+    int32_t rpieces;                     // reduction pieces per slab (0: no band is split)
+    int32_t nwg;                         // bucketing workgroups (runs) per (slab, level)
     int64_t cap;                         // list entries reserved per slab
+    int64_t part_per_slab;               // floats of partial tiles per slab
     int32_t rows[kMaxLevels];
     int32_t row_bands[kMaxLevels];
     int32_t cols[kMaxLevels];
@@ -61,6 +69,9 @@ struct TilePlan {
     int32_t chunks[kMaxLevels];
     int32_t band_begin[kMaxLevels];      // first band of level l within the slab
     int32_t job_begin[kMaxLevels + 1];
+    int32_t part_off[kMaxLevels];        // first partial-tile float of level l within the slab
+    int32_t rpieces_per_band[kMaxLevels];
+    int32_t rpiece_begin[kMaxLevels + 1];
 };
 
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).
@@ -106,6 +117,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
+
+// One element of storage type T as float32, and back (bfloat16: RNE).
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void store_f32(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_f32(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
 // Load VEC consecutive elements of storage type T as float32.
 template <typename T, int VEC> struct VecIO;

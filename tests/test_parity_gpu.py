@@ -41,7 +41,7 @@ def _gpu_forward(d, dev):
     return to_numpy(out)
 
 
-def _gpu_backward(d, dev, flags=(True, True, True)):
+def _gpu_backward(d, dev, flags=(True, True, True), **kw):
     from scale_deformable_attention_forward_amd import msda_backward
     import torch
     t = to_device(d, dev)
@@ -49,7 +49,7 @@ def _gpu_backward(d, dev, flags=(True, True, True)):
                         t["sampling_locations"], t["attention_weights"], d["value_layout"],
                         d["sampling_locations_layout"], d["align_corners"], d["padding_mode"],
                         compute_grad_value=flags[0], compute_grad_sampling_locations=flags[1],
-                        compute_grad_attention_weights=flags[2])
+                        compute_grad_attention_weights=flags[2], **kw)
     torch.cuda.synchronize()
     return tuple(to_numpy(r) for r in res)
 
@@ -228,9 +228,22 @@ def test_repeat_runs_are_stable(gpu_device):
     f1, f2 = _gpu_forward(d, gpu_device), _gpu_forward(d, gpu_device)
     np.testing.assert_array_equal(f1, f2)
     b1, b2 = _gpu_backward(d, gpu_device), _gpu_backward(d, gpu_device)
-    np.testing.assert_array_equal(b1[1], b2[1])   # grad_sampling_locations: no atomics
-    np.testing.assert_array_equal(b1[2], b2[2])   # grad_attention_weights: no atomics
-    compare("grad_value run to run", b1[0], b2[0], RTOL["fp32"])
+    for a, b in zip(b1, b2):
+        np.testing.assert_array_equal(a, b)   # destination-tiled grad_value: fixed summation order
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_split_bands_are_deterministic(dtype, gpu_device):
+    """Coarse levels whose bands are split over many workgroups (partial tiles
+    added in chunk order) give bitwise identical grad_value on every run."""
+    d = _mk(seed=19, levels=((20, 30), (5, 6), (2, 2)), N_q=6000, N_p=4, B=1, N_h=2, C_h=32,
+            value_dtype=dtype)
+    runs = [_gpu_backward(d, gpu_device, (True, False, False))[0] for _ in range(3)]
+    for r in runs[1:]:
+        np.testing.assert_array_equal(runs[0], r)
+    compare(f"split bands {dtype}", runs[0], oracle_backward(d, compute_grad_sampling_locations=False,
+                                                             compute_grad_attention_weights=False)[0],
+            RTOL[dtype])
 
 
 def test_autograd_function_matches_oracle(gpu_device):
@@ -264,3 +277,108 @@ def test_dense_coarse_levels(C_h, levels, N_q, N_p, B, N_h, gpu_device):
         d = _mk(seed=18, levels=levels, N_q=N_q, N_p=N_p, B=B, N_h=N_h, C_h=C_h, value_layout=vl, pad=pad)
         _check_backward(d, gpu_device, f"dense coarse C_h={C_h} {levels} {vl} {pad}")
         _check_backward(d, gpu_device, f"dense coarse grad_value only C_h={C_h}", (True, False, False))
+
+
+# ------------------------------------------------------- bfloat16 backward ---
+
+@pytest.mark.parametrize("mode", SWEEP, ids=lambda m: "-".join(map(str, m)))
+def test_backward_flag_sweep_bf16(mode, gpu_device):
+    vl, ll, align, pad = mode
+    d = _mk(seed=20, value_dtype="bf16", value_layout=vl, loc_layout=ll, align=align, pad=pad)
+    _check_backward(d, gpu_device, f"bf16 sweep {mode}")
+
+
+@pytest.mark.parametrize("C_h", [4, 6, 8, 32, 64, 100])
+def test_channel_counts_bf16_backward(C_h, gpu_device):
+    """C_h % 4 == 0 and <= 64 take the tiled path, the rest the generic one
+    (float32 accumulator in the workspace, converted once)."""
+    d = _mk(seed=21, C_h=C_h, N_q=29, N_h=2, value_dtype="bf16")
+    _check_backward(d, gpu_device, f"bf16 C_h={C_h}")
+
+
+def test_backward_bf16_square_workload_full_size(gpu_device):
+    """The bfloat16 BNLC / B2QHLP / align_corners / border workload's shapes
+    (B=4, 128/64/32/16 square pyramid, N_q = L = 21760) with a grad_output."""
+    wl = WORKLOADS[4]
+    d = make_inputs(wl.B, wl.levels, wl.L, wl.N_h, wl.C_h, wl.N_p, seed=4, loc_range=wl.loc_range,
+                    value_dtype="bf16", value_layout="BNLC", sampling_locations_layout="B2QHLP",
+                    grad_seed=24)
+    d.update(align_corners=True, padding_mode="border")
+    _check_backward(d, gpu_device, "bf16 square pyramid full size")
+
+
+def test_dense_coarse_levels_bf16(gpu_device):
+    d = _mk(seed=22, levels=((16, 20), (8, 10), (4, 5), (2, 3)), N_q=2000, N_p=4, B=2, N_h=2, C_h=32,
+            value_dtype="bf16", value_layout="BNLC")
+    _check_backward(d, gpu_device, "bf16 dense coarse")
+
+
+# --------------------------------------------------- accumulate into grad_value ---
+
+@pytest.mark.parametrize("dtype,C_h", [("fp32", 32), ("fp32", 6), ("bf16", 32), ("bf16", 6)])
+def test_accumulate_grad_value(dtype, C_h, gpu_device):
+    """grad_value += result: the old contents plus the oracle's gradient (both
+    the tiled path, C_h = 32, and the generic one, C_h = 6)."""
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward
+    d = _mk(seed=23, C_h=C_h, N_q=400, N_h=2, levels=((12, 14), (3, 4)), value_dtype=dtype)
+    t = to_device(d, gpu_device)
+    rng = np.random.default_rng(99)
+    init = rng.standard_normal(t["value"].shape).astype(np.float32)
+    gv = torch.from_numpy(init).to(gpu_device).to(t["value"].dtype)
+    init_used = to_numpy(gv).astype(np.float64)        # exact bf16 values when bf16
+    res = msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                        t["sampling_locations"], t["attention_weights"], grad_value=gv,
+                        accumulate_grad_value=True)
+    torch.cuda.synchronize()
+    assert res[0] is gv
+    want = oracle_backward(d)
+    compare(f"accumulated grad_value {dtype} C_h={C_h}", to_numpy(gv), init_used + want[0], RTOL[dtype])
+    compare(f"grad_loc with accumulate {dtype}", to_numpy(res[1]), want[1], RTOL[dtype])
+
+
+def test_accumulate_twice_equals_double(gpu_device):
+    """Two accumulating calls from zero give twice one call's gradient (the
+    chunked backward use: the same buffer collects several calls)."""
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward
+    d = _mk(seed=25, C_h=32, N_q=500, N_h=2)
+    t = to_device(d, gpu_device)
+    gv = torch.zeros_like(t["value"])
+    for _ in range(2):
+        msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                      t["sampling_locations"], t["attention_weights"], grad_value=gv,
+                      compute_grad_sampling_locations=False, compute_grad_attention_weights=False,
+                      accumulate_grad_value=True)
+    torch.cuda.synchronize()
+    want = oracle_backward(d, compute_grad_sampling_locations=False, compute_grad_attention_weights=False)[0]
+    compare("two accumulating calls", to_numpy(gv), 2.0 * want, RTOL["fp32"])
+
+
+def test_empty_problem_accumulate_leaves_grad_value(gpu_device):
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward
+    d = _mk(seed=26, N_q=0)
+    t = to_device(d, gpu_device)
+    gv = torch.full_like(t["value"], 3.0)
+    msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                  t["sampling_locations"], t["attention_weights"], grad_value=gv, accumulate_grad_value=True)
+    torch.cuda.synchronize()
+    assert bool((gv == 3.0).all().item())
+
+
+def test_unaligned_bf16_backward_takes_generic_path(gpu_device):
+    """A grad_value view one element into its allocation cannot take the tiled
+    path's 8-byte accesses; the generic path must give the same result."""
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward
+    d = _mk(seed=27, C_h=8, value_dtype="bf16")
+    t = to_device(d, gpu_device)
+    buf = torch.empty(t["value"].numel() + 1, dtype=torch.bfloat16, device=gpu_device)
+    gv = buf[1:].view(t["value"].shape)
+    res = msda_backward(t["grad_output"], t["value"], d["spatial_shapes"], d["level_start_index"],
+                        t["sampling_locations"], t["attention_weights"], grad_value=gv)
+    torch.cuda.synchronize()
+    want = oracle_backward(d)
+    for n, g, w in zip(("grad_value", "grad_loc", "grad_attn"), res, want):
+        compare(f"unaligned bf16 {n}", to_numpy(g), w, RTOL["bf16"])
