@@ -164,9 +164,12 @@ bool fast_backward_shape(const msda_problem& p)
     return true;
 }
 
-// Cut every level into bands (destination tiles) of rows x cols pixels: at
-// most kTilePixelsPerGroup pixels per lane group of the tile workgroup, at
-// most kTileBins anchor bins, at most kMaxBandsPerLevel bands per level. A
+// Cut every level into bands (destination tiles) of rows x cols pixels. A
+// tile is a grid of ny x nx lane-group rectangles (kRectRows x kRectCols
+// pixels each, ny * nx <= the groups of one tile workgroup) with at most
+// kTileBins anchor bins; of those shapes the one with the fewest tiles is
+// taken (then the fewest column bands: a sample is listed once per band its
+// 2x2 corner block touches). At most kMaxBandsPerLevel bands per level. A
 // band whose list is expected to hold more than two LDS passes of entries
 // (coarse levels, where many samples land on each pixel) is split into
 // chunks of its list, one workgroup each; each chunk writes a float32 partial
@@ -174,7 +177,8 @@ bool fast_backward_shape(const msda_problem& p)
 // Returns false if a level cannot be tiled that way.
 bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
 {
-    const int64_t pmax = (int64_t)(msda::kTileBlock / lpu) * msda::kTilePixelsPerGroup;
+    constexpr int64_t RH = msda::kRectRows, RW = msda::kRectCols;
+    const int64_t groups = msda::kTileBlock / lpu;
     const int64_t nsamp = p.N_q * p.N_p;
     const int64_t nwg = std::max<int64_t>(1, (nsamp + msda::kBandChunk - 1) / msda::kBandChunk);
     if (nwg >= 65536) return false;  // grid x of the bucketing kernels stays small
@@ -190,10 +194,21 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
             continue;
         }
         const int64_t H = p.spatial_shapes[2 * l], W = p.spatial_shapes[2 * l + 1];
-        const int64_t cols = std::min<int64_t>(W, std::min<int64_t>(pmax, msda::kTileBins / 2 - 1));
-        int64_t rows = std::max<int64_t>(1, std::min<int64_t>(H, pmax / cols));
-        while (rows > 1 && (rows + 1) * (cols + 1) > msda::kTileBins) --rows;
-        const int64_t rb = (H + rows - 1) / rows, cb = (W + cols - 1) / cols;
+        int64_t rows = 0, cols = 0, rb = 0, cb = 0;
+        const int64_t nx_max = std::min<int64_t>(groups, (W + RW - 1) / RW);
+        for (int64_t nx = 1; nx <= nx_max; ++nx) {
+            const int64_t ny = std::min<int64_t>(groups / nx, (H + RH - 1) / RH);
+            const int64_t r = std::min<int64_t>(H, ny * RH), c = std::min<int64_t>(W, nx * RW);
+            if ((r + 1) * (c + 1) > msda::kTileBins) continue;
+            const int64_t nrb = (H + r - 1) / r, ncb = (W + c - 1) / c;
+            if (rows == 0 || nrb * ncb < rb * cb || (nrb * ncb == rb * cb && ncb < cb)) {
+                rows = r;
+                cols = c;
+                rb = nrb;
+                cb = ncb;
+            }
+        }
+        if (rows == 0) return false;
         if (rb * cb > msda::kMaxBandsPerLevel) return false;
         // list entries of one band if locations spread evenly
         const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;

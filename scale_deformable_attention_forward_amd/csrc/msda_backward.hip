@@ -583,20 +583,24 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
     VecIO<T, 4>::store(dst, v);
 }
 
-// Tile kernel. LPU lanes per destination pixel (4 channels per lane),
-// kTileBlock / LPU pixel groups per workgroup, each owning up to
-// kTilePixelsPerGroup pixels of the tile.
+// Tile kernel. LPU lanes per lane group (4 channels per lane); each of the
+// kTileBlock / LPU groups owns a rectangle of kRectRows x kRectCols pixels of
+// the band. The entries anchored at a corner (x0, y0) reach the 2x2 pixels
+// (x0..x0+1, y0..y0+1), so a rectangle reads the (kRectRows + 1) x
+// (kRectCols + 1) anchor bins around it and loads each entry's grad_output
+// row once per bin, adding it to every pixel of the rectangle it reaches
+// (15 row loads per 8 pixels instead of 32 with one pixel per owner).
 template <typename T, int LPU>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
     float* __restrict__ partial, int accumulate)
 {
-    constexpr int NG = kTileBlock / LPU;
-    constexpr int PPG = kTilePixelsPerGroup;
+    constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
     __shared__ float4 s_ent[E];              // (fx, fy, A, q)
     __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
+    __shared__ uint32_t s_bkey[E];           // keys in binned order
     __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
     __shared__ uint16_t s_binned[E];         // staged entries grouped by bin (any order inside)
     __shared__ uint16_t s_sorted[E];         // staged entries ordered by (bin, k)
@@ -618,9 +622,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int local = job - t.job0;
     const int band = local / t.nch, chunk = local - band * t.nch;
     const BandRect br = band_rect(t, band);
-    const int r0 = br.r0, c0 = br.c0, tw = br.tw, P = br.tw * br.th;
+    const int r0 = br.r0, c0 = br.c0, tw = br.tw, th = br.th;
     const int nbw = tw + 1;                  // anchor bins cover rows r0-1..r1-1, cols c0-1..c1-1
-    const int nbins = (br.th + 1) * nbw;
+    const int nbins = (th + 1) * nbw;
     // this chunk's runs [w_lo, w_hi) of the band's list; run_off[w] is where run w starts
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
@@ -630,12 +634,17 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
-    const bool lane_ok = ch < g.Ch;
+    const int rects_x = (tw + RW - 1) / RW;
+    const int gy = grp / rects_x, gx = grp - gy * rects_x;
+    const int ry = gy * RH, rx = gx * RW;    // the group's rectangle, band-local
+    const bool grp_ok = ch < g.Ch && ry < th;
     const T* gl = grow0 + ch;
 
-    float4 acc[PPG];
+    float4 acc[RH][RW];
 #pragma unroll
-    for (int m = 0; m < PPG; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < RH; ++i)
+#pragma unroll
+        for (int j = 0; j < RW; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
 
     // A pass stages whole runs (at most E entries; one run never exceeds
     // kBandChunk <= E), so which entries share a pass does not depend on the
@@ -688,7 +697,11 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         }
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
         __syncthreads();
-        for (int i = tid; i < m_cnt; i += kTileBlock) s_binned[atomicAdd(&s_cursor[s_bin_of[i]], 1)] = (uint16_t)i;
+        for (int i = tid; i < m_cnt; i += kTileBlock) {
+            const int slot = atomicAdd(&s_cursor[s_bin_of[i]], 1);
+            s_binned[slot] = (uint16_t)i;
+            s_bkey[slot] = s_key[i];
+        }
         __syncthreads();
         // rank every entry among its bin by k (keys are unique within a band list)
         for (int i = tid; i < m_cnt; i += kTileBlock) {
@@ -696,25 +709,26 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             const uint32_t key = s_key[i];
             const int b0 = s_bstart[bin], b1 = s_bstart[bin + 1];
             int rank = 0;
-            for (int j = b0; j < b1; ++j) rank += s_key[s_binned[j]] < key ? 1 : 0;
+            for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
             s_sorted[b0 + rank] = (uint16_t)i;
         }
         __syncthreads();
-        // every pixel group sums its pixels' four neighbouring bins; partial sums
-        // per bin keep float32 rounding chains short
-        if (lane_ok) {
+        // every group walks the bins around its rectangle
+        if (grp_ok) {
 #pragma unroll
-            for (int m = 0; m < PPG; ++m) {
-                const int p = grp + m * NG;
-                if (p >= P) break;
-                const int py = p / tw, px = p - py * tw;
-                float4 pix = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 1
-                for (int corner = 0; corner < 4; ++corner) {
-                    const int dx = corner & 1, dy = corner >> 1;
-                    const int bin = (py + 1 - dy) * nbw + (px + 1 - dx);
+            for (int bi = 0; bi <= RH; ++bi) {
+#pragma unroll
+                for (int bj = 0; bj <= RW; ++bj) {
+                    const int by = ry + bi, bx = rx + bj;
+                    if (by > th || bx > tw) continue;  // no such bin
+                    const int bin = by * nbw + bx;
                     const int e1 = s_bstart[bin + 1];
-                    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+                    // per-bin partial sums keep float32 rounding chains short
+                    float4 bs[2][2];
+#pragma unroll
+                    for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+                        for (int dx = 0; dx < 2; ++dx) bs[dy][dx] = make_float4(0.f, 0.f, 0.f, 0.f);
                     for (int e = s_bstart[bin]; e < e1; e += 4) {
                         float4 ent[4];
                         float gv[4][4];
@@ -731,52 +745,69 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                         }
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const float wx = dx ? ent[u].x : 1.f - ent[u].x;
-                            const float wy = dy ? ent[u].y : 1.f - ent[u].y;
-                            const float coef = ent[u].z * (wx * wy);
-                            sum.x = __builtin_fmaf(coef, gv[u][0], sum.x);
-                            sum.y = __builtin_fmaf(coef, gv[u][1], sum.y);
-                            sum.z = __builtin_fmaf(coef, gv[u][2], sum.z);
-                            sum.w = __builtin_fmaf(coef, gv[u][3], sum.w);
+                            // corner (dx, dy) of an entry in bin (bi, bj) is pixel
+                            // (bi - 1 + dy, bj - 1 + dx) of the rectangle
+#pragma unroll
+                            for (int dy = 0; dy < 2; ++dy) {
+                                const int pr = bi - 1 + dy;
+                                if (pr < 0 || pr >= RH) continue;
+                                const float wy = ent[u].z * (dy ? ent[u].y : 1.f - ent[u].y);
+#pragma unroll
+                                for (int dx = 0; dx < 2; ++dx) {
+                                    const int pc = bj - 1 + dx;
+                                    if (pc < 0 || pc >= RW) continue;
+                                    const float coef = wy * (dx ? ent[u].x : 1.f - ent[u].x);
+                                    bs[dy][dx].x = __builtin_fmaf(coef, gv[u][0], bs[dy][dx].x);
+                                    bs[dy][dx].y = __builtin_fmaf(coef, gv[u][1], bs[dy][dx].y);
+                                    bs[dy][dx].z = __builtin_fmaf(coef, gv[u][2], bs[dy][dx].z);
+                                    bs[dy][dx].w = __builtin_fmaf(coef, gv[u][3], bs[dy][dx].w);
+                                }
+                            }
                         }
                     }
-                    pix.x += sum.x;
-                    pix.y += sum.y;
-                    pix.z += sum.z;
-                    pix.w += sum.w;
+#pragma unroll
+                    for (int dy = 0; dy < 2; ++dy) {
+                        const int pr = bi - 1 + dy;
+                        if (pr < 0 || pr >= RH) continue;
+#pragma unroll
+                        for (int dx = 0; dx < 2; ++dx) {
+                            const int pc = bj - 1 + dx;
+                            if (pc < 0 || pc >= RW) continue;
+                            acc[pr][pc].x += bs[dy][dx].x;
+                            acc[pr][pc].y += bs[dy][dx].y;
+                            acc[pr][pc].z += bs[dy][dx].z;
+                            acc[pr][pc].w += bs[dy][dx].w;
+                        }
+                    }
                 }
-                acc[m].x += pix.x;
-                acc[m].y += pix.y;
-                acc[m].z += pix.z;
-                acc[m].w += pix.w;
             }
         }
         __syncthreads();
     }
 
-    if (!lane_ok) return;
+    if (!grp_ok) return;
     if (t.nch == 1) {
         // the band's only job: store the final values
         const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
         T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
 #pragma unroll
-        for (int m = 0; m < PPG; ++m) {
-            const int p = grp + m * NG;
-            if (p >= P) break;
-            const int py = p / tw, px = p - py * tw;
-            store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[m], accumulate);
-        }
+        for (int i = 0; i < RH; ++i)
+#pragma unroll
+            for (int j = 0; j < RW; ++j)
+                if (ry + i < th && rx + j < tw)
+                    store_grad4(out + ((r0 + ry + i) * t.W + c0 + rx + j) * pstride + ch, acc[i][j], accumulate);
         return;
     }
-    // one chunk of a split band: its partial tile, pixel-major, C_h floats per pixel
+    // one chunk of a split band: its partial tile, pixel-major (band-local
+    // row-major pixel index), C_h floats per pixel
     float* slot = partial + (size_t)slab * tp.part_per_slab + t.part +
                   (size_t)(band * t.nch + chunk) * (t.R * t.CW) * g.Ch;
 #pragma unroll
-    for (int m = 0; m < PPG; ++m) {
-        const int p = grp + m * NG;
-        if (p >= P) break;
-        *reinterpret_cast<float4*>(slot + p * g.Ch + ch) = acc[m];
-    }
+    for (int i = 0; i < RH; ++i)
+#pragma unroll
+        for (int j = 0; j < RW; ++j)
+            if (ry + i < th && rx + j < tw)
+                *reinterpret_cast<float4*>(slot + ((ry + i) * tw + rx + j) * g.Ch + ch) = acc[i][j];
 }
 
 // Adds the partial tiles of split bands in chunk order and stores grad_value.
