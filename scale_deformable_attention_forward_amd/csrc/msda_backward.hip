@@ -175,15 +175,13 @@ __device__ __forceinline__ BwdRecord make_record(const Geometry& g, float ux, fl
     return r;
 }
 
-// Per-sample anchors for the destination-tiled grad_value pass, laid out
-// [b * N_h + h][l][q][p]: anchor corner packed (x0 + 2) | (y0 + 2) << 16
-// (x0, y0 >= -2 after the clamp above), the two fractions and the attention
-// weight.
+// Per-sample records for the destination-tiled grad_value pass, laid out
+// [b * N_h + h][l][q][p]: the anchor corner packed (x0 + 2) | (y0 + 2) << 16
+// (x0, y0 >= -2 after the clamp above) on its own for the bucketing kernels,
+// and (anchor bits, fx, fy, A) as one 16-byte record for the tile kernel.
 struct AnchorWs {
     uint32_t* anchor;
-    float* fx;
-    float* fy;
-    float* a;
+    float4* rec;
 };
 
 // Stage one record per (unit, sample) of the chunk [s0, s0 + sc).
@@ -209,10 +207,9 @@ __device__ __forceinline__ void stage_records(const Geometry& g, const float* __
             r = make_record(g, ux, uy, a, H, W, start, x0, y0);
             if (ws.anchor) {
                 const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
-                ws.anchor[k] = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
-                ws.fx[k] = r.fx;
-                ws.fy[k] = r.fy;
-                ws.a[k] = a;
+                const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
+                ws.anchor[k] = an;
+                ws.rec[k] = make_float4(__uint_as_float(an), r.fx, r.fy, a);
             }
         }
         s_rec[gi * row + s] = r;
@@ -331,19 +328,16 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 // ---------------------------------------------------------------------------
 // Fast path, grad_value by destination.
 //
-// Workspace views: per-sample arrays written by backward_fast_kernel, the
-// per-(slab, band, run) counts and offsets and the band lists (SoA, `cap`
-// entries reserved per slab; entry = sample index k = q * N_p + p within its
-// (slab, level), anchor, fractions, attention weight). Run w of a band holds
-// that band's samples among k in [w * kBandChunk, (w + 1) * kBandChunk).
+// Workspace views: the per-(slab, band, run) counts and offsets, the band
+// lists (`cap` entries reserved per slab; an entry is the sample index
+// k = q * N_p + p within its (slab, level)) and the per-sample records the
+// entries point at. Run w of a band holds that band's samples among k in
+// [w * kBandChunk, (w + 1) * kBandChunk).
 struct BandWs {
-    int* cnt;       // [slabs][bands][nwg]
-    int* off;       // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
+    int* cnt;            // [slabs][bands][nwg]
+    int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
     uint32_t* k;
-    uint32_t* anchor;
-    float* fx;
-    float* fy;
-    float* a;
+    const float4* rec;   // AnchorWs::rec
 };
 
 struct LevelTiles {
@@ -467,10 +461,7 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
 // Dynamic LDS: 2 * (max_bands + 1) ints, then max_entries (k, band) pairs
 // (kBandChunk samples times the most bands one sample can touch).
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
-                                                               const uint32_t* __restrict__ anchor,
-                                                               const float* __restrict__ sfx,
-                                                               const float* __restrict__ sfy,
-                                                               const float* __restrict__ sa, int max_bands,
+                                                               const uint32_t* __restrict__ anchor, int max_bands,
                                                                int max_entries)
 {
     constexpr int kWaves = kBandBlock / kWave;
@@ -539,12 +530,7 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     for (int i = tid; i < total; i += kBandBlock) {
         const int bnd = s_band[i];
         const size_t pos = lbase + run_off[(size_t)bnd * tp.nwg] + (i - loff[bnd]);
-        const uint32_t k = s_k[i];
-        w.k[pos] = k;
-        w.anchor[pos] = anchor[sbase + k];
-        w.fx[pos] = sfx[sbase + k];
-        w.fy[pos] = sfy[sbase + k];
-        w.a[pos] = sa[sbase + k];
+        w.k[pos] = s_k[i];
     }
 }
 
@@ -629,6 +615,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
     const size_t lbase = (size_t)slab * tp.cap;
+    const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
 
@@ -660,13 +647,13 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
         for (int i = tid; i < m_cnt; i += kTileBlock) {
-            const size_t pos = lbase + p0 + i;
+            const uint32_t k = w.k[lbase + p0 + i];
+            const float4 rc = srec[k];
             int x0, y0;
-            unpack_anchor(w.anchor[pos], x0, y0);
+            unpack_anchor(__float_as_uint(rc.x), x0, y0);
             const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            const uint32_t k = w.k[pos];
             const int q = (int)k / g.Np;
-            s_ent[i] = make_float4(w.fx[pos], w.fy[pos], w.a[pos], __int_as_float(q));
+            s_ent[i] = make_float4(rc.y, rc.z, rc.w, __int_as_float(q));
             s_key[i] = k;
             s_bin_of[i] = (uint16_t)bin;
             atomicAdd(&s_cursor[bin], 1);
@@ -886,7 +873,7 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const T* vslab = value + slab_off;
     float* gslab = gacc ? gacc + slab_off : nullptr;
     const T* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
-    const AnchorWs no_ws = {nullptr, nullptr, nullptr, nullptr};
+    const AnchorWs no_ws = {nullptr, nullptr};
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
@@ -1016,10 +1003,10 @@ static hipError_t launch_generic_t(const Geometry& g, const void* grad_out, cons
     return hipGetLastError();
 }
 
-// Workspace of the fast path with grad_value: per-sample arrays (16 bytes per
-// sample), per-(band, run) counts and offsets, the band lists (20 bytes per
-// reserved entry) and the float32 partial tiles of split bands. Every piece
-// starts 256-byte aligned.
+// Workspace of the fast path with grad_value: per-sample anchors and records
+// (20 bytes per sample), per-(band, run) counts and offsets, the band lists
+// (4 bytes per reserved entry) and the float32 partial tiles of split bands.
+// Every piece starts 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws,
@@ -1038,18 +1025,13 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     };
     AnchorWs a;
     a.anchor = reinterpret_cast<uint32_t*>(take(ns * 4));
-    a.fx = reinterpret_cast<float*>(take(ns * 4));
-    a.fy = reinterpret_cast<float*>(take(ns * 4));
-    a.a = reinterpret_cast<float*>(take(ns * 4));
+    a.rec = reinterpret_cast<float4*>(take(ns * 16));
     BandWs w;
     const size_t runs = nb * (size_t)tp.nwg;
     w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
     w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
     w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
-    w.anchor = reinterpret_cast<uint32_t*>(take(cap * 4));
-    w.fx = reinterpret_cast<float*>(take(cap * 4));
-    w.fy = reinterpret_cast<float*>(take(cap * 4));
-    w.a = reinterpret_cast<float*>(take(cap * 4));
+    w.rec = a.rec;
     float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
     if (bws) *bws = w;
@@ -1093,7 +1075,7 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                                 void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
                                 hipStream_t stream)
 {
-    AnchorWs ws = {nullptr, nullptr, nullptr, nullptr};
+    AnchorWs ws = {nullptr, nullptr};
     BandWs bw = {};
     float* partial = nullptr;
     if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw, &partial);
@@ -1117,8 +1099,8 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)fill_lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), fill_lds, stream, g, tp, bw, ws.anchor, ws.fx,
-                       ws.fy, ws.a, max_bands, max_entries);
+    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), fill_lds, stream, g, tp, bw, ws.anchor,
+                       max_bands, max_entries);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
