@@ -455,9 +455,10 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
 }
 
 // Bucketing 3/3: fill the band lists. Grid as band_count_kernel. Each
-// workgroup orders its entries by band in LDS and writes its run of every
-// band at the offset the scan gave it, with consecutive stores. (Order inside
-// a run is arbitrary; the tile pass orders what it sums.)
+// workgroup takes its run lengths from band_count_kernel, orders its entries
+// by band in LDS and writes its run of every band at the offset the scan gave
+// it, with consecutive stores. (Order inside a run is arbitrary; the tile
+// pass orders what it sums.)
 // Dynamic LDS: 2 * (max_bands + 1) ints, then max_entries (k, band) pairs
 // (kBandChunk samples times the most bands one sample can touch).
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
@@ -477,16 +478,11 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     const int nb = t.nbr * t.nbc;
     const int nsamp = g.Nq * g.Np;
     const int k0 = wg * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
-    for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
+    // this run's count of every band of the level, from band_count_kernel
+    const int* c = w.cnt + ((size_t)slab * tp.bands + t.band0) * tp.nwg + wg;
+    for (int i = tid; i < nb; i += kBandBlock) hist[i] = c[(size_t)i * tp.nwg];
     __syncthreads();
     const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
-    for (int k = k0 + tid; k < k1; k += kBandBlock) {
-        int x0, y0, bands[4];
-        unpack_anchor(anchor[sbase + k], x0, y0);
-        const int n = sample_bands(t, x0, y0, bands);
-        for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
-    }
-    __syncthreads();
     // exclusive scan of hist[0..nb) into loff, in rounds of kBandBlock bands
     const int lane = tid % kWave, wave = tid / kWave;
     int carry = 0;
