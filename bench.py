@@ -8,14 +8,18 @@ U[-0.05, 1.05], softmax attention weights, grad_output ~ N(0, 1). Inputs are
 seeded, synthetic, and resident in HBM before the timed region starts.
 
 Prints ONE JSON line. `value` is queries/s of whole steps; `roofline` is the
-dominant kernel's algorithmic bytes per launch over its average launch time
-(HIP events on the stream the kernels run on) against the 8 TB/s HBM peak;
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+dominant launch's algorithmic bytes over its average duration (HIP events on
+the stream the kernels run on) against the 8 TB/s HBM peak; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload on this host.
+
+`--report` instead times every named workload (forward, and backward where it
+has a grad_output) warm and with cold caches, next to the CPU oracle on all
+host cores and on one core, and prints one JSON line per workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,100 +35,239 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fp32_fwd_bwd_hbm_traffic.txt")
 METRIC = "queries/s and effective gathered HBM GB/s (% of peak), fwd+bwd, 1 MI355X"
 WORKLOAD_NUM = 5                # encoder shapes with grad_output (the forward uses the same arrays)
+BACKWARD_KERNELS = ("backward_fast_kernel", "band_count_kernel", "band_scan_kernel", "band_fill_kernel",
+                    "tile_scatter_kernel", "band_reduce_kernel")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--cold", action="store_true",
-                    help="also time steps with a 1 GiB scratch write between them (caches cold)")
+                    help="also time steps with a 1 GiB scratch write before each launch (caches cold)")
+    ap.add_argument("--report", action="store_true",
+                    help="time every named workload (GPU warm/cold, CPU oracle all cores / 1 core)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
 
 
-def inrange_corners(d):
-    """(sample, corner) pairs whose corner lies inside its level: the corners the
-    method must read. Float32 coordinate map as in the kernels."""
+# ------------------------------------------------------------ byte counts ---
+
+def _loc_bqhlp2(d):
     loc = d["sampling_locations"]
+    if d["sampling_locations_layout"] == "B2QHLP":
+        loc = np.moveaxis(loc, 1, -1)
+    return loc
+
+
+def counted_corners(d):
+    """(sample, corner) pairs the method must read: corner index inside its
+    level and bilinear weight nonzero (float32 coordinate map and border clamp
+    as in the kernels). Counted in numpy; independent of the GPU path."""
+    loc = _loc_bqhlp2(d)
+    align, border = bool(d["align_corners"]), d["padding_mode"] == "border"
     n = 0
     for l, (H, W) in enumerate(d["spatial_shapes"]):
         ux = loc[:, :, :, l, :, 0].astype(np.float64)
         uy = loc[:, :, :, l, :, 1].astype(np.float64)
-        # loc*W - 0.5 is exact in float64 here; one rounding to float32 = fmaf
-        x = (ux * W - 0.5).astype(np.float32)
-        y = (uy * H - 0.5).astype(np.float32)
-        x0 = np.floor(x).astype(np.int64)
-        y0 = np.floor(y).astype(np.int64)
-        for dx in (0, 1):
-            okx = (x0 + dx >= 0) & (x0 + dx < W)
-            for dy in (0, 1):
-                n += int((okx & (y0 + dy >= 0) & (y0 + dy < H)).sum())
+        if align:
+            x = (ux.astype(np.float32) * np.float32(W - 1)).astype(np.float32)
+            y = (uy.astype(np.float32) * np.float32(H - 1)).astype(np.float32)
+        else:   # u*W - 0.5 is exact in float64 here; one rounding to float32 = fmaf
+            x = (ux * W - 0.5).astype(np.float32)
+            y = (uy * H - 0.5).astype(np.float32)
+        if border:
+            x = np.clip(x, 0, W - 1)
+            y = np.clip(y, 0, H - 1)
+        x0, y0 = np.floor(x), np.floor(y)
+        fx, fy = x - x0, y - y0
+        x0, y0 = x0.astype(np.int64), y0.astype(np.int64)
+        for dx, wx in ((0, 1.0 - fx), (1, fx)):
+            okx = (x0 + dx >= 0) & (x0 + dx < W) & (wx != 0)
+            for dy, wy in ((0, 1.0 - fy), (1, fy)):
+                n += int((okx & (y0 + dy >= 0) & (y0 + dy < H) & (wy != 0)).sum())
     return n
 
 
 def byte_counts(d):
     """Algorithmic bytes per launch: nominal (4 corners per sample) and counted
-    (in-range corners only), plus the streams each kernel reads/writes once."""
+    (corners the method must read), plus the streams each launch reads or
+    writes once."""
     B, N_q, N_h, N_l, N_p = d["attention_weights"].shape
     C_h = d["value"].shape[-1]
-    s_v = 4
+    s_v = 2 if d["value_dtype"] == "bf16" else 4
     samples = B * N_q * N_h * N_l * N_p
     corner_bytes = C_h * s_v
-    inr = inrange_corners(d)
+    cnt = counted_corners(d)
     loc_b, attn_b = samples * 8, samples * 4
     out_b = B * N_q * N_h * C_h * s_v
     value_b = d["value"].size * s_v
     fwd_streams = loc_b + attn_b + out_b
-    # backward: grad_output + loc + attn in, grad_loc + grad_attn out, grad_value cleared once
+    # backward: grad_output + loc + attn in, grad_loc + grad_attn out, grad_value written once
     bwd_streams = out_b + loc_b + attn_b + loc_b + attn_b + value_b
     return {
         "samples": samples,
-        "inrange_corners": inr,
-        "inrange_fraction": inr / (4 * samples),
+        "counted_corners": cnt,
+        "counted_fraction": cnt / (4 * samples),
         "forward": {"nominal": 4 * samples * corner_bytes + fwd_streams,
-                    "counted": inr * corner_bytes + fwd_streams},
+                    "counted": cnt * corner_bytes + fwd_streams},
         # re-gather + scatter (read-modify-write counted once)
         "backward": {"nominal": 2 * 4 * samples * corner_bytes + bwd_streams,
-                     "counted": 2 * inr * corner_bytes + bwd_streams},
+                     "counted": 2 * cnt * corner_bytes + bwd_streams},
         "queries": B * N_q,
     }
 
 
 def measured_traffic():
     """HBM bytes per forward launch and per backward call, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by its copy calibration;
-    None for both when a kernel source changed since the counters were taken."""
-    import hashlib
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by its copy calibration
+    (per-dispatch bytes times dispatches per call), plus the L2 hit rate of each
+    kernel; (None, None, {}) when a kernel source changed since the counters
+    were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
-        return None, None
+        return None, None, {}
     for rel, digest in rec["sources_sha256"].items():
         path = os.path.join(ROOT, rel)
         if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
-            return None, None
+            return None, None, {}
     ff = rec["copy_calibration"]["fetch_factor"]
     wf = rec["copy_calibration"]["write_factor"]
     fwd = bwd = 0.0
+    per = {}
     for name, c in rec["per_dispatch"].items():
-        b = (c["FETCH_SIZE_KiB"] * ff + c["WRITE_SIZE_KiB"] * wf) * 1024.0
+        b = (c["FETCH_SIZE_KiB"] * ff + c["WRITE_SIZE_KiB"] * wf) * 1024.0 * c["dispatches_per_call"]
+        per[name] = {"hbm_bytes_per_call": b, "l2_hit_pct": c.get("L2_hit_pct")}
         if name.startswith("forward_kernel"):
             fwd += b
-        elif name.startswith("zero4_kernel"):
-            bwd += 2 * b   # the backward clears its band counters and grad_value
         else:
             bwd += b
+    return fwd, bwd, per
+
+
+# ------------------------------------------------------------------ timing ---
+
+def time_launches(fn, stream, iters, warmup, cold_buf=None):
+    """Per-launch durations (ms) from HIP events recorded on `stream` around
+    each launch; with cold_buf, the buffer is overwritten before every launch
+    (outside the events) to evict L2 and the Infinity Cache."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        if cold_buf is not None:
+            cold_buf.fill_(float(i))
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def stats(ms):
+    return {"ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)),
+            "ms_p10": float(np.percentile(ms, 10)), "ms_p90": float(np.percentile(ms, 90))}
+
+
+def _device_inputs(d, dev):
+    import torch
+    t = {}
+    if d["value_dtype"] == "bf16":
+        t["value"] = torch.from_numpy(d["value_bf16_bits"].view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    else:
+        t["value"] = torch.from_numpy(d["value"]).to(dev)
+    t["loc"] = torch.from_numpy(d["sampling_locations"]).to(dev)
+    t["attn"] = torch.from_numpy(d["attention_weights"]).to(dev)
+    if "grad_output" in d:
+        g = torch.from_numpy(d["grad_output"]).to(dev)
+        t["gout"] = g.to(torch.bfloat16) if d["value_dtype"] == "bf16" else g
+    return t
+
+
+def _launchers(d, t, stream):
+    """forward() and (if the workload has a grad_output) backward() closures
+    over pre-allocated outputs and workspace."""
+    import torch
+    from scale_deformable_attention_forward_amd import binding
+    ss, ls = d["spatial_shapes"], d["level_start_index"]
+    mode = (d["value_layout"], d["sampling_locations_layout"], d["align_corners"], d["padding_mode"])
+    B, N_q = d["attention_weights"].shape[:2]
+    N_h, C_h = d["attention_weights"].shape[2], d["value"].shape[-1]
+    out = torch.empty((B, N_q, N_h * C_h), dtype=t["value"].dtype, device=t["value"].device)
+
+    def fwd():
+        binding.msda_forward(t["value"], ss, ls, t["loc"], t["attn"], *mode, output=out, stream=stream)
+
+    bwd = None
+    if "gout" in t:
+        gv, gl, ga = torch.empty_like(t["value"]), torch.empty_like(t["loc"]), torch.empty_like(t["attn"])
+        nws = binding.backward_workspace_bytes(t["value"], ss, ls, t["loc"], *mode)
+        ws = torch.empty(max(1, nws), dtype=torch.uint8, device=t["value"].device)
+
+        def bwd():
+            binding.msda_backward(t["gout"], t["value"], ss, ls, t["loc"], t["attn"], *mode, grad_value=gv,
+                                  grad_sampling_locations=gl, grad_attention_weights=ga, workspace=ws,
+                                  stream=stream)
     return fwd, bwd
 
 
+# ------------------------------------------------------------ CPU oracle ---
+
+def _query_slice(d, nq):
+    """The first nq queries of a workload (same value pyramid)."""
+    s = dict(d)
+    s["attention_weights"] = d["attention_weights"][:, :nq]
+    if d["sampling_locations_layout"] == "B2QHLP":
+        s["sampling_locations"] = d["sampling_locations"][:, :, :nq]
+    else:
+        s["sampling_locations"] = d["sampling_locations"][:, :nq]
+    if "grad_output" in d:
+        s["grad_output"] = d["grad_output"][:, :nq]
+    return s
+
+
+def oracle_rate(d, passes, target_s, threads=None):
+    """Queries/s of the CPU oracle (fp64 C, OpenMP) running `passes` over
+    growing query slices of the workload until about target_s seconds; returns
+    (queries/s, threads used, description of the sample)."""
+    import oracle
+    prev = oracle.max_threads()
+    if threads is not None:
+        oracle.set_threads(threads)
+    used = oracle.max_threads()
+    B, N_q = d["attention_weights"].shape[:2]
+    args = dict(spatial_shapes=d["spatial_shapes"], level_start_index=d["level_start_index"],
+                value_layout=d["value_layout"], sampling_locations_layout=d["sampling_locations_layout"],
+                align_corners=d["align_corners"], padding_mode=d["padding_mode"])
+    nq, done_q, el = min(N_q, 64), 0, 0.0
+    while el < target_s:
+        s = _query_slice(d, nq)
+        t0 = time.perf_counter()
+        if "forward" in passes:
+            oracle.forward(d["value"], sampling_locations=s["sampling_locations"],
+                           attention_weights=s["attention_weights"], **args)
+        if "backward" in passes:
+            oracle.backward(s["grad_output"], d["value"], sampling_locations=s["sampling_locations"],
+                            attention_weights=s["attention_weights"], **args)
+        el += time.perf_counter() - t0
+        done_q += B * nq
+        if nq < N_q:
+            nq = min(N_q, nq * 4)
+    oracle.set_threads(prev)
+    return done_q / el, used, f"{done_q} queries of the workload ({'+'.join(passes)}, first-query slices " \
+                              f"up to the full N_q, {el:.1f} s), fp64 C oracle with OpenMP"
+
+
 def cpu_baseline(d, target_s):
-    """The CPU oracle (fp64, OpenMP) on the same inputs: whole forward+backward
-    steps, repeated until about target_s seconds have run."""
+    """The CPU oracle on the same inputs: whole forward+backward steps,
+    repeated until about target_s seconds have run."""
     import oracle
     args = (d["spatial_shapes"], d["level_start_index"])
     B, N_q = d["attention_weights"].shape[:2]
@@ -142,6 +285,53 @@ def cpu_baseline(d, target_s):
             "sample": f"{reps} full forward+backward step(s) of the same workload ({reps * B * N_q} "
                       f"queries, {el:.1f} s), fp64 C oracle with OpenMP"}
 
+
+# ---------------------------------------------------------------- report ---
+
+def report(a):
+    import torch
+    from scale_deformable_attention_forward_amd import binding
+    from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_inputs, make_workload
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    for num, wl in sorted(WORKLOADS.items()):
+        d = make_workload(num)
+        if "grad_output" not in d:
+            # backward timing on the same arrays, with a grad_output of its own seed
+            g = make_inputs(wl.B, wl.levels, wl.num_queries, wl.N_h, wl.C_h, wl.N_p, wl.seed,
+                            loc_dist=wl.loc_dist, loc_range=wl.loc_range, value_dtype=wl.value_dtype,
+                            value_layout=wl.value_layout, sampling_locations_layout=wl.sampling_locations_layout,
+                            grad_seed=1000 + num)
+            d["grad_output"] = g["grad_output"]
+        t = _device_inputs(d, dev)
+        fwd, bwd = _launchers(d, t, stream)
+        bc = byte_counts(d)
+        line = {"workload": num, "name": wl.name, "queries": bc["queries"],
+                "counted_corner_fraction": bc["counted_fraction"], "dtype": wl.value_dtype}
+        for name, fn in (("forward", fwd), ("backward", bwd)):
+            warm = time_launches(fn, stream, a.steps, a.warmup)
+            cold = time_launches(fn, stream, min(a.steps, 30), 2, cold_buf=scratch)
+            avg_s = float(np.mean(warm)) * 1e-3
+            line[name] = {
+                "warm": stats(warm), "cold": stats(cold),
+                "queries_per_s": bc["queries"] / avg_s,
+                "gbs_counted": bc[name]["counted"] / avg_s / 1e9,
+                "gbs_nominal": bc[name]["nominal"] / avg_s / 1e9,
+                "frac_of_hbm_peak_counted": bc[name]["counted"] / avg_s / 1e9 / HBM_PEAK_GBS,
+            }
+        if not a.no_cpu_baseline:
+            for name in ("forward", "backward"):
+                tgt = a.cpu_seconds / 4
+                qa, ca, sa = oracle_rate(d, (name,), tgt)
+                q1, c1, s1 = oracle_rate(d, (name,), tgt, threads=1)
+                line[name]["cpu_oracle"] = {"all_cores": {"queries_per_s": qa, "cores": ca, "sample": sa},
+                                            "one_core": {"queries_per_s": q1, "cores": c1, "sample": s1}}
+        print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------------ main ---
 
 def main():
     a = parse()
@@ -161,6 +351,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4, "launches": 5}), flush=True)
         return
+    if a.report:
+        report(a)
+        return
     from scale_deformable_attention_forward_amd import binding
     from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_workload
 
@@ -168,24 +361,9 @@ def main():
     wl = WORKLOADS[WORKLOAD_NUM]
     d = make_workload(WORKLOAD_NUM)
     dev = torch.device("cuda:0")
-    v = torch.from_numpy(d["value"]).to(dev)
-    loc = torch.from_numpy(d["sampling_locations"]).to(dev)
-    attn = torch.from_numpy(d["attention_weights"]).to(dev)
-    gout = torch.from_numpy(d["grad_output"]).to(dev)
-    out = torch.empty(gout.shape, dtype=torch.float32, device=dev)
-    gv = torch.empty_like(v)
-    gl = torch.empty_like(loc)
-    ga = torch.empty_like(attn)
-    ss, ls = d["spatial_shapes"], d["level_start_index"]
-    ws = torch.empty(max(1, binding.backward_workspace_bytes(v, ss, ls, loc)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-
-    def fwd():
-        binding.msda_forward(v, ss, ls, loc, attn, output=out, stream=stream)
-
-    def bwd():
-        binding.msda_backward(gout, v, ss, ls, loc, attn, grad_value=gv, grad_sampling_locations=gl,
-                              grad_attention_weights=ga, workspace=ws, stream=stream)
+    t = _device_inputs(d, dev)
+    fwd, bwd = _launchers(d, t, stream)
 
     for _ in range(a.warmup):
         fwd()
@@ -212,22 +390,8 @@ def main():
     cold = None
     if a.cold:
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        cf, cb = [], []
-        for i in range(min(K, 20)):
-            scratch.fill_(float(i))
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record(stream)
-            fwd()
-            e[1].record(stream)
-            scratch.fill_(float(i) + 0.5)
-            e2 = torch.cuda.Event(enable_timing=True)
-            e2.record(stream)
-            bwd()
-            e[2].record(stream)
-            torch.cuda.synchronize()
-            cf.append(e[0].elapsed_time(e[1]))
-            cb.append(e2.elapsed_time(e[2]))
-        cold = {"forward_ms_median": float(np.median(cf)), "backward_ms_median": float(np.median(cb))}
+        cold = {"forward": stats(time_launches(fwd, stream, min(K, 30), 2, cold_buf=scratch)),
+                "backward": stats(time_launches(bwd, stream, min(K, 30), 2, cold_buf=scratch))}
         del scratch
 
     bc = byte_counts(d)
@@ -237,21 +401,20 @@ def main():
         avg_s = float(np.mean(ms)) * 1e-3
         nominal = bc[name]["nominal"]
         counted = bc[name]["counted"]
-        return {
-            "ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)),
-            "ms_p10": float(np.percentile(ms, 10)), "ms_p90": float(np.percentile(ms, 90)),
+        r = stats(ms)
+        r.update({
             "queries_per_s": Q / avg_s,
             "bytes_nominal": nominal, "bytes_counted": counted,
             "gbs_nominal": nominal / avg_s / 1e9, "gbs_counted": counted / avg_s / 1e9,
             "frac_counted": counted / avg_s / 1e9 / HBM_PEAK_GBS,
-        }
+        })
+        return r
 
     kf, kb = kernel_line("forward", f_ms), kernel_line("backward", b_ms)
-    t_fwd, t_bwd = measured_traffic()
+    t_fwd, t_bwd, per_kernel = measured_traffic()
     kf["traffic"], kb["traffic"] = t_fwd, t_bwd
     kf["launch"] = "forward_kernel (1 launch)"
-    kb["launch"] = ("msda_backward call: backward_fast_kernel, zero4_kernel x2, band_count_kernel, "
-                    "band_scan_kernel, band_fill_kernel, tile_scatter_kernel")
+    kb["launch"] = "msda_backward call: " + ", ".join(BACKWARD_KERNELS)
     dom_name, dom = ("backward", kb) if kb["ms_mean"] >= kf["ms_mean"] else ("forward", kf)
     achieved = dom["bytes_nominal"] / (dom["ms_mean"] * 1e-3) / 1e9
     roofline = {
@@ -260,8 +423,8 @@ def main():
         "bytes_per_launch": dom["bytes_nominal"],
         "launch": dom["launch"],
         "note": "achieved = algorithmic bytes (nominal per-query figure x queries, 4 corners per sample) "
-                "/ mean HIP-event time of one launch; achieved_counted uses in-range corners only; "
-                "traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles/)",
+                "/ mean HIP-event time of one launch; achieved_counted uses the corners the method must "
+                "read; traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles/)",
         "achieved_counted": dom["gbs_counted"],
     }
     res = {
@@ -283,7 +446,8 @@ def main():
                    "global_batch": wl.B, "queries_per_step": Q, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {"forward": kf, "backward": kb},
-        "inrange_corner_fraction": bc["inrange_fraction"],
+        "per_kernel_counters": per_kernel,
+        "counted_corner_fraction": bc["counted_fraction"],
         "wall_s_timed": wall,
     }
     if cold is not None:

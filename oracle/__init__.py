@@ -67,12 +67,20 @@ def bind(path):
     lib.oracle_count_inrange_corners.restype = i64
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_set_threads.restype = None
     return lib
 
 
 def max_threads() -> int:
     """Threads the oracle's OpenMP loops use on this host."""
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for later oracle calls (for timing; the results do not depend on it:
+    every output element is summed by one thread in a fixed order)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _f64(a):

@@ -290,3 +290,6 @@ int64_t oracle_count_inrange_corners(int64_t B, int64_t L, int64_t Nq, int64_t N
 
 /* Threads an OpenMP region of this library uses (for reporting only). */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* Threads later oracle calls use (timing only; results do not depend on it). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -406,3 +406,21 @@ def test_oracle_rejects_inconsistent_level_table():
     with pytest.raises(ValueError):
         oracle.forward(d["value"], d["spatial_shapes"], (0, 1, 2), d["sampling_locations"],
                        d["attention_weights"])
+
+
+def test_results_do_not_depend_on_thread_count():
+    """Every output element is summed by one thread in a fixed order, so the
+    oracle's results are bitwise the same on one thread and on many (the
+    one-core and all-core timings of the benchmark run the same arithmetic)."""
+    d = _tiny(seed=31, N_q=40, grad_seed=32)
+    many = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        assert oracle.max_threads() == 1
+        f1, b1 = _fwd(d, False, "zeros"), _bwd(d, False, "zeros")
+    finally:
+        oracle.set_threads(many)
+    fn, bn = _fwd(d, False, "zeros"), _bwd(d, False, "zeros")
+    np.testing.assert_array_equal(f1, fn)
+    for a, b in zip(b1, bn):
+        np.testing.assert_array_equal(a, b)
