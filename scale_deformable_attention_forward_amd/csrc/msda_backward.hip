@@ -394,6 +394,19 @@ __device__ __forceinline__ void unpack_anchor(uint32_t a, int& x0, int& y0)
     y0 = (int)(a >> 16) - 2;
 }
 
+// The anchors of this thread's samples k0 + tid + i * kBandBlock of one run,
+// all loads issued before any is used (0xffffffff past the run's end).
+constexpr int kRunPerThread = kBandChunk / kBandBlock;
+__device__ __forceinline__ void load_run_anchors(const uint32_t* __restrict__ an, int k0, int k1,
+                                                 uint32_t (&a)[kRunPerThread])
+{
+#pragma unroll
+    for (int i = 0; i < kRunPerThread; ++i) {
+        const int k = k0 + (int)threadIdx.x + i * kBandBlock;
+        a[i] = k < k1 ? an[k] : 0xffffffffu;
+    }
+}
+
 // Bucketing 1/3: per-(slab, band, run) sample counts. Grid (run, level,
 // slab); every workgroup writes the counts of all bands of its level, so the
 // array needs no clearing.
@@ -409,10 +422,13 @@ __global__ __launch_bounds__(kBandBlock) void band_count_kernel(Geometry g, Tile
     const int k0 = wg * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
     for (int i = threadIdx.x; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
-    const uint32_t* an = anchor + (size_t)(slab * g.Nl + l) * nsamp;
-    for (int k = k0 + threadIdx.x; k < k1; k += kBandBlock) {
+    uint32_t a[kRunPerThread];
+    load_run_anchors(anchor + (size_t)(slab * g.Nl + l) * nsamp, k0, k1, a);
+#pragma unroll
+    for (int i = 0; i < kRunPerThread; ++i) {
+        if (a[i] == 0xffffffffu) continue;
         int x0, y0, bands[4];
-        unpack_anchor(an[k], x0, y0);
+        unpack_anchor(a[i], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
         for (int j = 0; j < n; ++j) atomicAdd(&hist[bands[j]], 1);
     }
@@ -481,8 +497,10 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     // this run's count of every band of the level, from band_count_kernel
     const int* c = w.cnt + ((size_t)slab * tp.bands + t.band0) * tp.nwg + wg;
     for (int i = tid; i < nb; i += kBandBlock) hist[i] = c[(size_t)i * tp.nwg];
-    __syncthreads();
     const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
+    uint32_t a[kRunPerThread];
+    load_run_anchors(anchor + sbase, k0, k1, a);
+    __syncthreads();
     // exclusive scan of hist[0..nb) into loff, in rounds of kBandBlock bands
     const int lane = tid % kWave, wave = tid / kWave;
     int carry = 0;
@@ -509,9 +527,12 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     if (tid == 0) loff[nb] = carry;
     for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
     __syncthreads();
-    for (int k = k0 + tid; k < k1; k += kBandBlock) {
+#pragma unroll
+    for (int i = 0; i < kRunPerThread; ++i) {
+        if (a[i] == 0xffffffffu) continue;
+        const int k = k0 + tid + i * kBandBlock;
         int x0, y0, bands[4];
-        unpack_anchor(anchor[sbase + k], x0, y0);
+        unpack_anchor(a[i], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
         for (int j = 0; j < n; ++j) {
             const int slot = loff[bands[j]] + atomicAdd(&hist[bands[j]], 1);
@@ -642,9 +663,25 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         // stage a pass of list entries and count them per anchor bin
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
-        for (int i = tid; i < m_cnt; i += kTileBlock) {
-            const uint32_t k = w.k[lbase + p0 + i];
-            const float4 rc = srec[k];
+        constexpr int kStage = kTileEntries / kTileBlock;
+        uint32_t kk[kStage];
+        float4 rcs[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            kk[u] = i < m_cnt ? w.k[lbase + p0 + i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            rcs[u] = i < m_cnt ? srec[kk[u]] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            if (i >= m_cnt) continue;
+            const uint32_t k = kk[u];
+            const float4 rc = rcs[u];
             int x0, y0;
             unpack_anchor(__float_as_uint(rc.x), x0, y0);
             const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
