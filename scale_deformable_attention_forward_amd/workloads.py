@@ -165,3 +165,42 @@ def make_workload(wl: Workload | int, grad_seed=None):
                     sampling_locations_layout=wl.sampling_locations_layout, grad_seed=g)
     d.update(align_corners=wl.align_corners, padding_mode=wl.padding_mode)
     return d
+
+
+def make_producer_inputs(B, levels, N_q, N_h, N_p, D, seed, value_dtype="fp32", offset_pixels=2.0,
+                         grad_seed=None):
+    """Draw the inputs of the producer of sampling locations and attention
+    weights: query features ~ N(0, 1) of shape (B, N_q, D), reference points
+    U[0, 1] of shape (B, N_q, N_l, 2), an offset projection (N_h*N_l*N_p*2, D)
+    whose outputs are about `offset_pixels` pixels, an attention projection
+    (N_h*N_l*N_p, D) with logits of about unit size, and small biases. With
+    value_dtype "bf16" the query and both projections are rounded to bfloat16
+    (``*_bf16_bits`` hold the patterns; the float32 arrays hold their exact
+    values). With grad_seed, also N(0, 1) gradients for the two outputs.
+    """
+    levels = tuple((int(h), int(w)) for h, w in levels)
+    N_l = len(levels)
+    S = N_l * N_p
+    rng = np.random.default_rng(seed)
+    out = {
+        "query": rng.standard_normal((B, N_q, D)).astype(np.float32),
+        "reference_points": rng.uniform(0.0, 1.0, size=(B, N_q, N_l, 2)).astype(np.float32),
+        "offset_weight": (rng.standard_normal((N_h * S * 2, D)) * (offset_pixels / np.sqrt(D))).astype(np.float32),
+        "offset_bias": rng.normal(0.0, offset_pixels, size=N_h * S * 2).astype(np.float32),
+        "attention_weight": (rng.standard_normal((N_h * S, D)) / np.sqrt(D)).astype(np.float32),
+        "attention_bias": rng.normal(0.0, 0.1, size=N_h * S).astype(np.float32),
+    }
+    if value_dtype == "bf16":
+        for k in ("query", "offset_weight", "attention_weight"):
+            bits = bf16_round_bits(out[k])
+            out[k] = bf16_bits_to_f32(bits)
+            out[k + "_bf16_bits"] = bits
+    elif value_dtype != "fp32":
+        raise ValueError(f"unknown value dtype {value_dtype!r}")
+    out.update(spatial_shapes=levels, level_start_index=level_start_index(levels), N_h=N_h, N_p=N_p, D=D,
+               value_dtype=value_dtype)
+    if grad_seed is not None:
+        g = np.random.default_rng(grad_seed)
+        out["grad_sampling_locations"] = g.standard_normal((B, N_q, N_h, N_l, N_p, 2)).astype(np.float32)
+        out["grad_attention_weights"] = g.standard_normal((B, N_q, N_h, N_l, N_p)).astype(np.float32)
+    return out
