@@ -1,12 +1,19 @@
 /*
  * msda.h - C ABI of the gfx950 (MI355X) multi-scale deformable attention library.
  *
- * Two operations, each a call below:
+ * Operations, each a call below:
  *   msda_forward   - "MS Deformable Attention Kernel API Reference"
  *                    (Background; Parameters; Returns).
  *   msda_backward  - "MS Deformable Attention Backward Kernel API Reference"
  *                    (Background; Parameters: grad_output and the
  *                    compute_grad_* flags; Returns; Notes).
+ *   msda_producer_forward, msda_fused_forward, msda_producer_backward -
+ *                    the step that feeds the sampler: "MS Deformable
+ *                    Attention Kernel API Reference" (Background) samples at
+ *                    learned sampling locations with attention weights; these
+ *                    calls produce them from per-query features (a linear
+ *                    projection, the per-level normalisation and the softmax
+ *                    written out below), alone or fused with the sampler.
  *
  * Notation follows the pages: B batch, N_q queries, N_h heads, C_h channels
  * per head, N_l pyramid levels, N_p sampling points per (query, head, level),
@@ -37,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MSDA_ABI_VERSION 2
+#define MSDA_ABI_VERSION 3
 #define MSDA_MAX_LEVELS 16
 
 typedef enum msda_status {
@@ -179,6 +186,84 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
                           void* grad_value, float* grad_sampling_locations,
                           float* grad_attention_weights, unsigned int flags, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Producer of the sampler's inputs. For query row m = (b, q) with features
+ * x_m = query[b, q, :] (D elements) and S = N_l * N_p:
+ *   off[m, h, l, p, c] = x_m . offset_weight[((h*N_l + l)*N_p + p)*2 + c, :]
+ *                        + offset_bias[same row]            (c = 0: x, 1: y; pixels)
+ *   z[m, h, l, p]      = x_m . attention_weight[(h*N_l + l)*N_p + p, :]
+ *                        + attention_bias[same row]
+ *   sampling_locations[b, q, h, l, p, x] = reference_points[b, q, l, x] + off[m, h, l, p, x] / W_l
+ *   sampling_locations[b, q, h, l, p, y] = reference_points[b, q, l, y] + off[m, h, l, p, y] / H_l
+ *   attention_weights[b, q, h, :, :]     = softmax over the S logits z[m, h, :, :]
+ * (the pages leave how the locations and weights are learned open; this is
+ * the plain reading: offsets in pixels of their level, normalised by the
+ * level's size, around per-level reference points).
+ *
+ *   query               (B, N_q, D), value_dtype, row-major
+ *   reference_points    (B, N_q, N_l, 2), float32, normalised (x, y)
+ *   offset_weight       (N_h * N_l * N_p * 2, D), value_dtype (out_features, in_features)
+ *   offset_bias         (N_h * N_l * N_p * 2), float32, or NULL (zero)
+ *   attention_weight    (N_h * N_l * N_p, D), value_dtype
+ *   attention_bias      (N_h * N_l * N_p), float32, or NULL (zero)
+ * problem->L, C_h and value_layout describe the value tensor of the sampler
+ * (msda_fused_forward); the producer alone only needs them to be valid.
+ * Supported: 1 <= D, N_l * N_p <= 64 (<= 32 for msda_fused_forward),
+ * M * D < 2^31 (M = B * N_q); otherwise MSDA_ERR_UNSUPPORTED. Products are
+ * float32 on the matrix cores (bfloat16 inputs widened exactly); the softmax
+ * and the normalisation are float32.
+ */
+msda_status msda_producer_forward(const msda_problem* problem, int64_t D, const void* query,
+                                  const float* reference_points, const void* offset_weight,
+                                  const float* offset_bias, const void* attention_weight,
+                                  const float* attention_bias, float* sampling_locations,
+                                  float* attention_weights, hipStream_t stream);
+
+/*
+ * msda_producer_forward followed by msda_forward in one kernel: output as
+ * msda_forward computes it from the locations and weights msda_producer_forward
+ * computes (the same float32 values, so the result is bitwise that of the two
+ * calls). sampling_locations and attention_weights are outputs here and may
+ * each be NULL (not stored; a backward needs them). value and output as in
+ * msda_forward.
+ */
+msda_status msda_fused_forward(const msda_problem* problem, int64_t D, const void* query,
+                               const float* reference_points, const void* offset_weight,
+                               const float* offset_bias, const void* attention_weight,
+                               const float* attention_bias, const void* value, void* output,
+                               float* sampling_locations, float* attention_weights, hipStream_t stream);
+
+/* Bytes of device workspace msda_producer_backward needs (float32 partial
+   weight gradients of row chunks; 0 when no weight or bias gradient is
+   possible). */
+msda_status msda_producer_backward_workspace_size(const msda_problem* problem, int64_t D, size_t* bytes);
+
+/*
+ * Backward of msda_producer_forward. Inputs: query, offset_weight and
+ * attention_weight as in the forward; attention_weights = the forward's
+ * output; grad_sampling_locations (sampling-location layout) and
+ * grad_attention_weights (B, N_q, N_h, N_l, N_p), float32, each NULL for a
+ * zero gradient. With G_off = grad_loc / (W_l or H_l) and
+ * G_z = A * (grad_A - sum over the head's S entries of A * grad_A):
+ *   grad_query[m, :]          = G_off[m] . offset_weight + G_z[m] . attention_weight   (value_dtype)
+ *   grad_reference_points[m, l, c] = sum over (h, p) of grad_sampling_locations[m, h, l, p, c]
+ *   grad_offset_weight        = G_off^T . X,  grad_offset_bias    = column sums of G_off
+ *   grad_attention_weight     = G_z^T . X,    grad_attention_bias = column sums of G_z
+ * (weight and bias gradients float32). Every output may be NULL (skipped);
+ * all six NULL returns MSDA_ERR_NOTHING_TO_COMPUTE. Outputs are overwritten.
+ * Every sum has a fixed order: results are bitwise reproducible. workspace:
+ * 16-byte aligned device memory of msda_producer_backward_workspace_size bytes
+ * (may be NULL when no weight or bias gradient is asked for).
+ */
+msda_status msda_producer_backward(const msda_problem* problem, int64_t D, const void* query,
+                                   const void* offset_weight, const void* attention_weight,
+                                   const float* attention_weights, const float* grad_sampling_locations,
+                                   const float* grad_attention_weights, void* grad_query,
+                                   float* grad_reference_points, float* grad_offset_weight,
+                                   float* grad_offset_bias, float* grad_attention_weight,
+                                   float* grad_attention_bias, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* msda_status_string(msda_status status);

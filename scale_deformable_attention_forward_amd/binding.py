@@ -8,7 +8,9 @@ if the library is missing or a call fails, an exception is raised.
 Keyword names and defaults follow "MS Deformable Attention Kernel API
 Reference" (API Reference: ms_deformable_attention) and "MS Deformable
 Attention Backward Kernel API Reference" (API Reference:
-ms_deformable_attention_bwd).
+ms_deformable_attention_bwd). The producer calls (sampling locations and
+attention weights from query features, alone or fused with the sampler) take
+the names of the C declarations in include/msda.h.
 """
 from __future__ import annotations
 
@@ -30,12 +32,13 @@ VALUE_LAYOUTS = {"BLNC": 0, "BNLC": 1}
 LOC_LAYOUTS = {"BQHLP2": 0, "B2QHLP": 1}
 PADDINGS = {"zeros": 0, "border": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 BACKWARD_ACCUMULATE_GRAD_VALUE = 1  # msda_backward flag: grad_value += result
 
 # Every symbol include/msda.h declares.
 EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
-                    "msda_status_string", "msda_abi_version")
+                    "msda_producer_forward", "msda_fused_forward", "msda_producer_backward_workspace_size",
+                    "msda_producer_backward", "msda_status_string", "msda_abi_version")
 
 
 class MsdaProblem(ctypes.Structure):
@@ -75,6 +78,15 @@ def load_library(path: str = LIB_PATH):
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward_workspace_size.argtypes = [pp, ctypes.POINTER(sz)]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.msda_producer_forward.argtypes = [pp, i64] + [vp] * 8 + [vp]
+    lib.msda_producer_forward.restype = ctypes.c_int
+    lib.msda_fused_forward.argtypes = [pp, i64] + [vp] * 10 + [vp]
+    lib.msda_fused_forward.restype = ctypes.c_int
+    lib.msda_producer_backward_workspace_size.argtypes = [pp, i64, ctypes.POINTER(sz)]
+    lib.msda_producer_backward_workspace_size.restype = ctypes.c_int
+    lib.msda_producer_backward.argtypes = [pp, i64] + [vp] * 12 + [vp, sz, vp]
+    lib.msda_producer_backward.restype = ctypes.c_int
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
@@ -299,3 +311,220 @@ def backward_workspace_bytes(value, spatial_shapes, level_start_index, sampling_
     _raise_for(lib, lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
                "msda_backward_workspace_size")
     return n.value
+
+
+# ------------------------------------------------------------------ producer ---
+
+def _producer_shapes(query, reference_points, offset_weight, attention_weight, spatial_shapes, N_h):
+    """(B, N_q, D, N_l, N_p) of a producer call, with its shape checks."""
+    if query.dim() != 3:
+        raise ValueError("query must have shape (B, N_q, D)")
+    B, N_q, D = query.shape
+    N_l = len(spatial_shapes)
+    rows = attention_weight.shape[0] if attention_weight.dim() == 2 else -1
+    if rows <= 0 or rows % (N_h * N_l):
+        raise ValueError("attention_weight must have shape (N_h * N_l * N_p, D)")
+    N_p = rows // (N_h * N_l)
+    if tuple(attention_weight.shape) != (N_h * N_l * N_p, D):
+        raise ValueError("attention_weight must have shape (N_h * N_l * N_p, D)")
+    if tuple(offset_weight.shape) != (N_h * N_l * N_p * 2, D):
+        raise ValueError("offset_weight must have shape (N_h * N_l * N_p * 2, D)")
+    if tuple(reference_points.shape) != (B, N_q, N_l, 2):
+        raise ValueError("reference_points must have shape (B, N_q, N_l, 2)")
+    return B, N_q, D, N_l, N_p
+
+
+def _check_optional(t, name, shape, dtype):
+    if t is None:
+        return
+    _check_tensor(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+
+
+def _producer_inputs(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias,
+                     N_h, N_l, N_p):
+    _check_tensor(query, "query", query.dtype)
+    if query.dtype not in DTYPES:
+        raise ValueError(f"query dtype {query.dtype} not supported (float32 or bfloat16)")
+    _check_tensor(reference_points, "reference_points", torch.float32)
+    _check_tensor(offset_weight, "offset_weight", query.dtype)
+    _check_tensor(attention_weight, "attention_weight", query.dtype)
+    _check_optional(offset_bias, "offset_bias", (N_h * N_l * N_p * 2,), torch.float32)
+    _check_optional(attention_bias, "attention_bias", (N_h * N_l * N_p,), torch.float32)
+
+
+def _sampling_shape(B, N_q, N_h, N_l, N_p, layout):
+    if layout == "BQHLP2":
+        return (B, N_q, N_h, N_l, N_p, 2)
+    if layout == "B2QHLP":
+        return (B, 2, N_q, N_h, N_l, N_p)
+    raise ValueError(f"unknown sampling_locations_layout {layout!r}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def msda_producer_forward(query, reference_points, offset_weight, offset_bias, attention_weight,
+                          attention_bias, spatial_shapes, level_start_index, num_heads,
+                          sampling_locations_layout="BQHLP2", sampling_locations=None,
+                          attention_weights=None, stream=None):
+    """Sampling locations (in the requested layout) and attention weights
+    (B, N_q, N_h, N_l, N_p) from query features: returns (locations, weights)."""
+    lib = load_library()
+    N_h = int(num_heads)
+    B, N_q, D, N_l, N_p = _producer_shapes(query, reference_points, offset_weight, attention_weight,
+                                           spatial_shapes, N_h)
+    _producer_inputs(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias,
+                     N_h, N_l, N_p)
+    loc_shape = _sampling_shape(B, N_q, N_h, N_l, N_p, sampling_locations_layout)
+    if sampling_locations is None:
+        sampling_locations = torch.empty(loc_shape, dtype=torch.float32, device=query.device)
+    _check_optional(sampling_locations, "sampling_locations", loc_shape, torch.float32)
+    if attention_weights is None:
+        attention_weights = torch.empty((B, N_q, N_h, N_l, N_p), dtype=torch.float32, device=query.device)
+    _check_optional(attention_weights, "attention_weights", (B, N_q, N_h, N_l, N_p), torch.float32)
+    L = sum(int(h) * int(w) for h, w in spatial_shapes)
+    prob, keep = make_problem(B, L, N_q, N_h, 1, spatial_shapes, level_start_index, N_p, "BLNC",
+                              sampling_locations_layout, False, "zeros", query.dtype)
+    st = lib.msda_producer_forward(ctypes.byref(prob), D, query.data_ptr(), reference_points.data_ptr(),
+                                   offset_weight.data_ptr(), _ptr(offset_bias), attention_weight.data_ptr(),
+                                   _ptr(attention_bias), sampling_locations.data_ptr(),
+                                   attention_weights.data_ptr(), _stream_ptr(stream))
+    _raise_for(lib, st, "msda_producer_forward")
+    return sampling_locations, attention_weights
+
+
+def msda_fused_forward(value, spatial_shapes, level_start_index, query, reference_points, offset_weight,
+                       offset_bias, attention_weight, attention_bias, value_layout="BLNC",
+                       sampling_locations_layout="BQHLP2", align_corners=False, padding_mode="zeros",
+                       return_sampling=False, output=None, stream=None):
+    """Producer and sampler in one kernel: returns the (B, N_q, N_h * C_h)
+    output, or (output, sampling_locations, attention_weights) with
+    ``return_sampling`` (what a backward needs)."""
+    lib = load_library()
+    if value.dim() != 4:
+        raise ValueError("value must be 4-D")
+    if value_layout == "BLNC":
+        Bv, L, N_h, C_h = value.shape
+    elif value_layout == "BNLC":
+        Bv, N_h, L, C_h = value.shape
+    else:
+        raise ValueError(f"unknown value_layout {value_layout!r}")
+    B, N_q, D, N_l, N_p = _producer_shapes(query, reference_points, offset_weight, attention_weight,
+                                           spatial_shapes, N_h)
+    if Bv != B:
+        raise ValueError("query and value differ in batch size")
+    _check_tensor(value, "value", query.dtype)
+    _producer_inputs(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias,
+                     N_h, N_l, N_p)
+    if output is None:
+        output = torch.empty((B, N_q, N_h * C_h), dtype=value.dtype, device=value.device)
+    _check_optional(output, "output", (B, N_q, N_h * C_h), value.dtype)
+    loc = attn = None
+    if return_sampling:
+        loc = torch.empty(_sampling_shape(B, N_q, N_h, N_l, N_p, sampling_locations_layout),
+                          dtype=torch.float32, device=value.device)
+        attn = torch.empty((B, N_q, N_h, N_l, N_p), dtype=torch.float32, device=value.device)
+    prob, keep = make_problem(B, L, N_q, N_h, C_h, spatial_shapes, level_start_index, N_p, value_layout,
+                              sampling_locations_layout, align_corners, padding_mode, value.dtype)
+    st = lib.msda_fused_forward(ctypes.byref(prob), D, query.data_ptr(), reference_points.data_ptr(),
+                                offset_weight.data_ptr(), _ptr(offset_bias), attention_weight.data_ptr(),
+                                _ptr(attention_bias), value.data_ptr(), output.data_ptr(), _ptr(loc),
+                                _ptr(attn), _stream_ptr(stream))
+    _raise_for(lib, st, "msda_fused_forward")
+    return (output, loc, attn) if return_sampling else output
+
+
+PRODUCER_GRADS = ("query", "reference_points", "offset_weight", "offset_bias", "attention_weight",
+                  "attention_bias")
+
+
+def msda_producer_backward(query, offset_weight, attention_weight, attention_weights,
+                           grad_sampling_locations, grad_attention_weights, spatial_shapes,
+                           level_start_index, sampling_locations_layout="BQHLP2", compute=PRODUCER_GRADS,
+                           workspace=None, stream=None):
+    """Gradients of the producer's inputs (dict keyed by PRODUCER_GRADS; only
+    the names in ``compute`` are computed, the others are None). Either output
+    gradient may be None (zero)."""
+    lib = load_library()
+    if attention_weights.dim() != 5:
+        raise ValueError("attention_weights must have shape (B, N_q, N_h, N_l, N_p)")
+    B, N_q, N_h, N_l, N_p = attention_weights.shape
+    if N_l != len(spatial_shapes):
+        raise ValueError("attention_weights and spatial_shapes differ in level count")
+    if query.dim() != 3 or tuple(query.shape[:2]) != (B, N_q):
+        raise ValueError("query must have shape (B, N_q, D)")
+    D = query.shape[2]
+    _check_tensor(query, "query", query.dtype)
+    if query.dtype not in DTYPES:
+        raise ValueError(f"query dtype {query.dtype} not supported (float32 or bfloat16)")
+    _check_optional(offset_weight, "offset_weight", (N_h * N_l * N_p * 2, D), query.dtype)
+    _check_optional(attention_weight, "attention_weight", (N_h * N_l * N_p, D), query.dtype)
+    _check_tensor(attention_weights, "attention_weights", torch.float32)
+    loc_shape = _sampling_shape(B, N_q, N_h, N_l, N_p, sampling_locations_layout)
+    _check_optional(grad_sampling_locations, "grad_sampling_locations", loc_shape, torch.float32)
+    _check_optional(grad_attention_weights, "grad_attention_weights", (B, N_q, N_h, N_l, N_p), torch.float32)
+    unknown = set(compute) - set(PRODUCER_GRADS)
+    if unknown:
+        raise ValueError(f"unknown gradients {sorted(unknown)}")
+    dev = query.device
+    shapes = {"query": (query.shape, query.dtype), "reference_points": ((B, N_q, N_l, 2), torch.float32),
+              "offset_weight": (offset_weight.shape, torch.float32),
+              "offset_bias": ((N_h * N_l * N_p * 2,), torch.float32),
+              "attention_weight": (attention_weight.shape, torch.float32),
+              "attention_bias": ((N_h * N_l * N_p,), torch.float32)}
+    out = {k: (torch.empty(shapes[k][0], dtype=shapes[k][1], device=dev) if k in compute else None)
+           for k in PRODUCER_GRADS}
+    L = sum(int(h) * int(w) for h, w in spatial_shapes)
+    prob, keep = make_problem(B, L, N_q, N_h, 1, spatial_shapes, level_start_index, N_p, "BLNC",
+                              sampling_locations_layout, False, "zeros", query.dtype)
+    n = ctypes.c_size_t(0)
+    _raise_for(lib, lib.msda_producer_backward_workspace_size(ctypes.byref(prob), D, ctypes.byref(n)),
+               "msda_producer_backward_workspace_size")
+    ws = None
+    if n.value and any(out[k] is not None for k in PRODUCER_GRADS[2:]):
+        if workspace is not None:
+            if workspace.device != dev or workspace.numel() * workspace.element_size() < n.value:
+                raise ValueError(f"workspace must be a GPU tensor of at least {n.value} bytes")
+            ws = workspace
+        else:
+            ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    ws_len = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.msda_producer_backward(ctypes.byref(prob), D, query.data_ptr(), offset_weight.data_ptr(),
+                                    attention_weight.data_ptr(), attention_weights.data_ptr(),
+                                    _ptr(grad_sampling_locations), _ptr(grad_attention_weights),
+                                    *(_ptr(out[k]) for k in PRODUCER_GRADS), _ptr(ws), ws_len,
+                                    _stream_ptr(stream))
+    _raise_for(lib, st, "msda_producer_backward")
+    return out
+
+
+class MSDAProducer(torch.autograd.Function):
+    """torch.autograd wrapper of the producer: forward and backward both run in libmsda.so.
+    Returns (sampling_locations, attention_weights)."""
+
+    @staticmethod
+    def forward(ctx, query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias,
+                spatial_shapes, level_start_index, num_heads, sampling_locations_layout="BQHLP2"):
+        loc, attn = msda_producer_forward(query, reference_points, offset_weight, offset_bias,
+                                          attention_weight, attention_bias, spatial_shapes,
+                                          level_start_index, num_heads, sampling_locations_layout)
+        ctx.cfg = (tuple(map(tuple, spatial_shapes)), tuple(level_start_index), sampling_locations_layout)
+        ctx.save_for_backward(query, offset_weight, attention_weight, attn)
+        return loc, attn
+
+    @staticmethod
+    def backward(ctx, grad_loc, grad_attn):
+        query, w_off, w_att, attn = ctx.saved_tensors
+        ss, ls, layout = ctx.cfg
+        need = ctx.needs_input_grad[:6]
+        names = [k for k, n in zip(PRODUCER_GRADS, need) if n]
+        if not names:
+            return (None,) * 10
+        g = msda_producer_backward(query, w_off, w_att, attn,
+                                   None if grad_loc is None else grad_loc.contiguous(),
+                                   None if grad_attn is None else grad_attn.contiguous(), ss, ls, layout,
+                                   compute=names)
+        return tuple(g[k] for k in PRODUCER_GRADS) + (None,) * 4

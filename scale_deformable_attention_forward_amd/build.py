@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsda.so")
-SOURCES = ["msda_api.hip", "msda_forward.hip", "msda_backward.hip"]
+SOURCES = ["msda_api.hip", "msda_forward.hip", "msda_backward.hip", "msda_producer.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -13,6 +13,7 @@
 
 #include "../../include/msda.h"
 #include "msda_device.h"
+#include "msda_producer.h"
 
 namespace msda {
 hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
@@ -258,6 +259,82 @@ size_t generic_workspace_bytes(const msda_problem& p, const Sizes& z)
     return p.value_dtype == MSDA_BF16 ? (size_t)z.value_elems * 4 : 0;
 }
 
+// Outputs [o] must not overlap any input or each other (NULL entries skipped).
+struct Span {
+    const void* p;
+    size_t n;
+};
+bool spans_disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins)
+{
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlap(o->p, o->n, i.p, i.n)) return false;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(o->p, o->n, o2->p, o2->n)) return false;
+    }
+    return true;
+}
+
+// Producer geometry and the byte sizes of its tensors.
+struct ProducerSizes {
+    size_t query, ref, w_off, b_off, w_att, b_att;
+};
+
+msda_status check_producer(const msda_problem* p, int64_t D, bool fused, Geometry* g, Sizes* z,
+                           msda::ProducerGeom* pg, ProducerSizes* ps)
+{
+    const msda_status st = check_problem(p, g, z);
+    if (st != MSDA_OK) return st;
+    if (D < 1) return MSDA_ERR_INVALID_ARGUMENT;
+    const int64_t S = (int64_t)g->S;
+    if (S > (fused ? msda::kPFusedMaxSamples : msda::kPMaxSamples)) return MSDA_ERR_UNSUPPORTED;
+    int64_t M, qe, we;
+    if (!mul_ok(p->B, p->N_q, &M) || !mul_ok(M, D, &qe) || qe >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    if (!mul_ok(p->N_h * 3 * S, D + 1, &we) || we >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    if (M * p->N_l * 2 >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    ps->query = (size_t)qe * z->elem;
+    ps->ref = (size_t)M * p->N_l * 2 * 4;
+    ps->w_off = (size_t)p->N_h * S * 2 * D * z->elem;
+    ps->b_off = (size_t)p->N_h * S * 2 * 4;
+    ps->w_att = (size_t)p->N_h * S * D * z->elem;
+    ps->b_att = (size_t)p->N_h * S * 4;
+    pg->M = (int32_t)M;
+    pg->D = (int32_t)D;
+    pg->S = (int32_t)S;
+    pg->Nh = g->Nh;
+    pg->Nl = g->Nl;
+    pg->Np = g->Np;
+    pg->Nq = g->Nq;
+    pg->ct = (int32_t)((3 * S + 15) / 16);
+    pg->tpr = std::max(4, 1 << ilog2((int)S));
+    pg->b2q = g->b2q;
+    pg->loc_pair_aligned = 0;
+    pg->vec = 1;
+    // weight gradients: about 1024 workgroups of (row chunk, head, 64 columns)
+    const int64_t per_chunk = p->N_h * ((D + 63) / 64);
+    const int64_t target = std::max<int64_t>(1, 1024 / std::max<int64_t>(1, per_chunk));
+    int64_t rows = (std::max<int64_t>(M, 1) + target - 1) / target;
+    rows = std::max<int64_t>(32, (rows + 31) / 32 * 32);
+    pg->mrows = (int32_t)std::min<int64_t>(rows, kIndexLimit / 2);
+    pg->mchunks = (int32_t)std::max<int64_t>(1, (M + pg->mrows - 1) / pg->mrows);
+    return MSDA_OK;
+}
+
+// 4-element row loads for the projection operands when D and the pointers allow.
+int producer_vec(int64_t D, int elem, std::initializer_list<const void*> ptrs)
+{
+    if (D % 4) return 1;
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 4 * (size_t)elem)) return 1;
+    return 4;
+}
+
+msda::ProducerArgsRaw producer_args(const void* query, const float* ref, const void* w_off, const float* b_off,
+                                    const void* w_att, const float* b_att)
+{
+    return msda::ProducerArgsRaw{query, ref, w_off, b_off, w_att, b_att};
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,6 +466,155 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
                                           attention_weights, grad_value, grad_sampling_locations,
                                           grad_attention_weights, workspace, stream);
     }
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+msda_status msda_producer_forward(const msda_problem* problem, int64_t D, const void* query,
+                                  const float* reference_points, const void* offset_weight, const float* offset_bias,
+                                  const void* attention_weight, const float* attention_bias,
+                                  float* sampling_locations, float* attention_weights, hipStream_t stream)
+{
+    Geometry g;
+    Sizes z;
+    msda::ProducerGeom pg;
+    ProducerSizes ps;
+    const msda_status st = check_producer(problem, D, false, &g, &z, &pg, &ps);
+    if (st != MSDA_OK) return st;
+    if (pg.M == 0) return MSDA_OK;
+    if (!query || !reference_points || !offset_weight || !attention_weight || !sampling_locations ||
+        !attention_weights)
+        return MSDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(query, z.elem) || !aligned(offset_weight, z.elem) || !aligned(attention_weight, z.elem) ||
+        !aligned(reference_points, 4) || !aligned(offset_bias, 4) || !aligned(attention_bias, 4) ||
+        !aligned(sampling_locations, 4) || !aligned(attention_weights, 4))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    if (!spans_disjoint({{sampling_locations, loc_bytes}, {attention_weights, attn_bytes}},
+                        {{query, ps.query}, {reference_points, ps.ref}, {offset_weight, ps.w_off},
+                         {offset_bias, ps.b_off}, {attention_weight, ps.w_att}, {attention_bias, ps.b_att}}))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    pg.vec = producer_vec(D, z.elem, {query, offset_weight, attention_weight});
+    pg.loc_pair_aligned = aligned(sampling_locations, 8);
+    const hipError_t e = msda::launch_producer_forward(
+        g, pg, problem->value_dtype == MSDA_BF16,
+        producer_args(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias),
+        sampling_locations, attention_weights, stream);
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+msda_status msda_fused_forward(const msda_problem* problem, int64_t D, const void* query,
+                               const float* reference_points, const void* offset_weight, const float* offset_bias,
+                               const void* attention_weight, const float* attention_bias, const void* value,
+                               void* output, float* sampling_locations, float* attention_weights, hipStream_t stream)
+{
+    Geometry g;
+    Sizes z;
+    msda::ProducerGeom pg;
+    ProducerSizes ps;
+    const msda_status st = check_producer(problem, D, true, &g, &z, &pg, &ps);
+    if (st != MSDA_OK) return st;
+    if (pg.M == 0) return MSDA_OK;
+    if (!query || !reference_points || !offset_weight || !attention_weight || !value || !output)
+        return MSDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(query, z.elem) || !aligned(offset_weight, z.elem) || !aligned(attention_weight, z.elem) ||
+        !aligned(value, z.elem) || !aligned(output, z.elem) || !aligned(reference_points, 4) ||
+        !aligned(offset_bias, 4) || !aligned(attention_bias, 4) || !aligned(sampling_locations, 4) ||
+        !aligned(attention_weights, 4))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    if (!spans_disjoint({{output, z.out_bytes}, {sampling_locations, loc_bytes}, {attention_weights, attn_bytes}},
+                        {{query, ps.query}, {reference_points, ps.ref}, {offset_weight, ps.w_off},
+                         {offset_bias, ps.b_off}, {attention_weight, ps.w_att}, {attention_bias, ps.b_att},
+                         {value, z.value_bytes}}))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)g.B * g.Nh * ((g.Nq + 63) / 64) >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    // the sampler's lane layout, as in msda_forward
+    const int vec = pick_vec(problem->C_h, z.elem, {value, output});
+    const int lanes = (int)std::min<int64_t>(64, (problem->C_h + vec - 1) / vec);
+    g.lpu_log2 = ilog2(lanes);
+    const int64_t per_chunk = ((int64_t)1 << g.lpu_log2) * vec;
+    g.chunks = (int32_t)((problem->C_h + per_chunk - 1) / per_chunk);
+    g.units = 0;
+    g.blocks = 0;
+    pg.vec = producer_vec(D, z.elem, {query, offset_weight, attention_weight});
+    pg.loc_pair_aligned = sampling_locations && aligned(sampling_locations, 8);
+    const hipError_t e = msda::launch_fused_forward(
+        g, pg, problem->value_dtype == MSDA_BF16, vec,
+        producer_args(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias), value,
+        output, sampling_locations, attention_weights, stream);
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+msda_status msda_producer_backward_workspace_size(const msda_problem* problem, int64_t D, size_t* bytes)
+{
+    if (!bytes) return MSDA_ERR_INVALID_ARGUMENT;
+    Geometry g;
+    Sizes z;
+    msda::ProducerGeom pg;
+    ProducerSizes ps;
+    const msda_status st = check_producer(problem, D, false, &g, &z, &pg, &ps);
+    if (st != MSDA_OK) return st;
+    *bytes = pg.M == 0 ? 0 : msda::producer_bwd_workspace_floats(pg) * sizeof(float);
+    return MSDA_OK;
+}
+
+msda_status msda_producer_backward(const msda_problem* problem, int64_t D, const void* query,
+                                   const void* offset_weight, const void* attention_weight,
+                                   const float* attention_weights, const float* grad_sampling_locations,
+                                   const float* grad_attention_weights, void* grad_query,
+                                   float* grad_reference_points, float* grad_offset_weight, float* grad_offset_bias,
+                                   float* grad_attention_weight, float* grad_attention_bias, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
+{
+    Geometry g;
+    Sizes z;
+    msda::ProducerGeom pg;
+    ProducerSizes ps;
+    const msda_status st = check_producer(problem, D, false, &g, &z, &pg, &ps);
+    if (st != MSDA_OK) return st;
+    const bool want_w = grad_offset_weight || grad_offset_bias || grad_attention_weight || grad_attention_bias;
+    if (!grad_query && !grad_reference_points && !want_w) return MSDA_ERR_NOTHING_TO_COMPUTE;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    const std::initializer_list<Span> outs = {{grad_query, ps.query}, {grad_reference_points, ps.ref},
+                                              {grad_offset_weight, ps.w_off / z.elem * 4},
+                                              {grad_offset_bias, ps.b_off},
+                                              {grad_attention_weight, ps.w_att / z.elem * 4},
+                                              {grad_attention_bias, ps.b_att}};
+    for (const Span& o : outs)
+        if (o.p && !aligned(o.p, o.p == grad_query ? (size_t)z.elem : 4)) return MSDA_ERR_INVALID_ARGUMENT;
+    if (pg.M == 0) {
+        // no rows: the weight and bias gradients are sums over nothing
+        hipError_t e = hipSuccess;
+        for (const Span& o : {outs.begin()[2], outs.begin()[3], outs.begin()[4], outs.begin()[5]})
+            if (o.p && e == hipSuccess) e = msda::launch_zero_elems(const_cast<void*>(o.p), (int64_t)(o.n / 4), 4, stream);
+        return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+    }
+    if (!query || !offset_weight || !attention_weight || !attention_weights) return MSDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(query, z.elem) || !aligned(offset_weight, z.elem) || !aligned(attention_weight, z.elem) ||
+        !aligned(attention_weights, 4) || !aligned(grad_sampling_locations, 4) || !aligned(grad_attention_weights, 4))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const std::initializer_list<Span> ins = {{query, ps.query}, {offset_weight, ps.w_off},
+                                             {attention_weight, ps.w_att}, {attention_weights, attn_bytes},
+                                             {grad_sampling_locations, loc_bytes},
+                                             {grad_attention_weights, attn_bytes}};
+    if (!spans_disjoint(outs, ins)) return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t need = msda::producer_bwd_workspace_floats(pg) * sizeof(float);
+    if (want_w) {
+        if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
+        for (const Span& s : ins)
+            if (overlap(workspace, need, s.p, s.n)) return MSDA_ERR_INVALID_ARGUMENT;
+        for (const Span& s : outs)
+            if (overlap(workspace, need, s.p, s.n)) return MSDA_ERR_INVALID_ARGUMENT;
+    }
+    pg.vec = producer_vec(D, z.elem, {query, offset_weight, attention_weight});
+    const msda::ProducerGradIn in{attention_weights, grad_attention_weights, grad_sampling_locations};
+    const msda::ProducerGradOut out{grad_query, grad_reference_points, grad_offset_weight, grad_offset_bias,
+                                    grad_attention_weight, grad_attention_bias};
+    const hipError_t e = msda::launch_producer_backward(
+        g, pg, problem->value_dtype == MSDA_BF16,
+        producer_args(query, nullptr, offset_weight, nullptr, attention_weight, nullptr), in, out,
+        want_w ? workspace : nullptr, stream);
     return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
 }
 

@@ -200,4 +200,85 @@ template <int VEC> struct VecIO<uint16_t, VEC> {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Forward sampling of one unit, shared by the sampler and the fused
+// producer + sampler kernels.
+
+// Gather record of one sample: the anchor corner's pixel and its level's row
+// length (the four bilinear weights travel beside it as a float4).
+struct FwdRecordPix {
+    int32_t pix;   // flat pixel index (along L) of corner (x0, y0)
+    int32_t W;     // row length of the sample's level, in pixels
+};
+
+// Coordinate map, padding and bilinear corners of one sample at normalised
+// (ux, uy) of level (H, W, start) with attention weight a: w holds the four
+// corner weights (x0,y0), (x0+1,y0), (x0,y0+1), (x0+1,y0+1) premultiplied by
+// a, 0 for a corner outside the level.
+__device__ __forceinline__ void sampler_record(const Geometry& g, float ux, float uy, float a, int H, int W,
+                                               int start, float4& w, FwdRecordPix& rp)
+{
+    float x = pixel_coord(ux, W, g.align_corners);
+    float y = pixel_coord(uy, H, g.align_corners);
+    if (g.border) {
+        // clamp into the level before taking corners (NaN lands on 0)
+        x = fminf(fmaxf(x, 0.f), (float)(W - 1));
+        y = fminf(fmaxf(y, 0.f), (float)(H - 1));
+    } else {
+        // anything past [-1, W] reads nothing; keeps the int conversion safe
+        x = fminf(fmaxf(x, -2.f), (float)(W + 1));
+        y = fminf(fmaxf(y, -2.f), (float)(H + 1));
+    }
+    const float x0f = floorf(x), y0f = floorf(y);
+    const float fx = x - x0f, fy = y - y0f;
+    const int x0 = (int)x0f, y0 = (int)y0f;
+    // corner column / row inside the level
+    const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
+    const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
+    const float gx = 1.f - fx, gy = 1.f - fy;
+    w.x = (ix0 && iy0) ? a * (gx * gy) : 0.f;
+    w.y = (ix1 && iy0) ? a * (fx * gy) : 0.f;
+    w.z = (ix0 && iy1) ? a * (gx * fy) : 0.f;
+    w.w = (ix1 && iy1) ? a * (fx * fy) : 0.f;
+    rp.pix = start + y0 * W + x0;
+    rp.W = W;
+}
+
+// Accumulate sc staged samples of one unit into acc: VEC channels per lane,
+// loading only the corners whose weight is nonzero. `slab` points at the
+// lane's first channel of the unit's (b, h) slab; pstride is the element
+// distance between neighbouring pixels.
+template <typename T, int VEC>
+__device__ __forceinline__ void gather_samples(const T* slab, int pstride, const float4* rw,
+                                               const FwdRecordPix* rpix, int sc, float (&acc)[VEC])
+{
+#pragma unroll 4
+    for (int s = 0; s < sc; ++s) {
+        const float4 w = rw[s];
+        const FwdRecordPix rp = rpix[s];
+        const T* p00 = slab + rp.pix * pstride;
+        float v[VEC];
+        if (w.x != 0.f) {
+            VecIO<T, VEC>::load(p00, v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.x, v[i], acc[i]);
+        }
+        if (w.y != 0.f) {
+            VecIO<T, VEC>::load(p00 + pstride, v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.y, v[i], acc[i]);
+        }
+        if (w.z != 0.f) {
+            VecIO<T, VEC>::load(p00 + rp.W * pstride, v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.z, v[i], acc[i]);
+        }
+        if (w.w != 0.f) {
+            VecIO<T, VEC>::load(p00 + (rp.W + 1) * pstride, v);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.w, v[i], acc[i]);
+        }
+    }
+}
+
 }  // namespace msda

@@ -23,11 +23,6 @@
 
 namespace msda {
 
-struct FwdRecordPix {
-    int32_t pix;   // flat pixel index (along L) of corner (x0, y0)
-    int32_t W;     // row length of the sample's level, in pixels
-};
-
 template <typename T, int VEC>
 __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
                                                          const T* __restrict__ value,
@@ -99,68 +94,14 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
                     ux = loc[2 * idx];
                     uy = loc[2 * idx + 1];
                 }
-                const float a = attn[idx];
-                float x = pixel_coord(ux, W, g.align_corners);
-                float y = pixel_coord(uy, H, g.align_corners);
-                if (g.border) {
-                    // clamp into the level before taking corners (NaN lands on 0)
-                    x = fminf(fmaxf(x, 0.f), (float)(W - 1));
-                    y = fminf(fmaxf(y, 0.f), (float)(H - 1));
-                } else {
-                    // anything past [-1, W] reads nothing; keeps the int conversion safe
-                    x = fminf(fmaxf(x, -2.f), (float)(W + 1));
-                    y = fminf(fmaxf(y, -2.f), (float)(H + 1));
-                }
-                const float x0f = floorf(x), y0f = floorf(y);
-                const float fx = x - x0f, fy = y - y0f;
-                const int x0 = (int)x0f, y0 = (int)y0f;
-                // corner column / row inside the level
-                const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
-                const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
-                const float gx = 1.f - fx, gy = 1.f - fy;
-                w.x = (ix0 && iy0) ? a * (gx * gy) : 0.f;
-                w.y = (ix1 && iy0) ? a * (fx * gy) : 0.f;
-                w.z = (ix0 && iy1) ? a * (gx * fy) : 0.f;
-                w.w = (ix1 && iy1) ? a * (fx * fy) : 0.f;
-                rp.pix = start + y0 * W + x0;
-                rp.W = W;
+                sampler_record(g, ux, uy, attn[idx], H, W, start, w, rp);
             }
             s_w[gi * row + s] = w;
             s_pix[gi * row + s] = rp;
         }
         __syncthreads();
         // ---- gather: VEC channels per lane, only corners with nonzero weight ----
-        if (active) {
-            const float4* rw = s_w + grp * row;
-            const FwdRecordPix* rpix = s_pix + grp * row;
-#pragma unroll 4
-            for (int s = 0; s < sc; ++s) {
-                const float4 w = rw[s];
-                const FwdRecordPix rp = rpix[s];
-                const T* p00 = slab + rp.pix * pstride;
-                float v[VEC];
-                if (w.x != 0.f) {
-                    VecIO<T, VEC>::load(p00, v);
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.x, v[i], acc[i]);
-                }
-                if (w.y != 0.f) {
-                    VecIO<T, VEC>::load(p00 + pstride, v);
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.y, v[i], acc[i]);
-                }
-                if (w.z != 0.f) {
-                    VecIO<T, VEC>::load(p00 + rp.W * pstride, v);
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.z, v[i], acc[i]);
-                }
-                if (w.w != 0.f) {
-                    VecIO<T, VEC>::load(p00 + (rp.W + 1) * pstride, v);
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.w, v[i], acc[i]);
-                }
-            }
-        }
+        if (active) gather_samples<T, VEC>(slab, pstride, s_w + grp * row, s_pix + grp * row, sc, acc);
     }
     if (active) VecIO<T, VEC>::store(out + ((b * g.Nq + q) * g.Nh + h) * g.Ch + c0, acc);
 }

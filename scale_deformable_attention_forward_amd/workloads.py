@@ -168,7 +168,7 @@ def make_workload(wl: Workload | int, grad_seed=None):
 
 
 def make_producer_inputs(B, levels, N_q, N_h, N_p, D, seed, value_dtype="fp32", offset_pixels=2.0,
-                         grad_seed=None):
+                         grad_seed=None, dyadic=False):
     """Draw the inputs of the producer of sampling locations and attention
     weights: query features ~ N(0, 1) of shape (B, N_q, D), reference points
     U[0, 1] of shape (B, N_q, N_l, 2), an offset projection (N_h*N_l*N_p*2, D)
@@ -177,19 +177,35 @@ def make_producer_inputs(B, levels, N_q, N_h, N_p, D, seed, value_dtype="fp32", 
     value_dtype "bf16" the query and both projections are rounded to bfloat16
     (``*_bf16_bits`` hold the patterns; the float32 arrays hold their exact
     values). With grad_seed, also N(0, 1) gradients for the two outputs.
+
+    dyadic=True draws coarse dyadic numbers instead (query integers in
+    [-2, 2], offset weights k/64 and attention weights k/256 with integer
+    |k| <= 4, biases k/64, reference points k/256): for D <= 64 every product
+    and partial sum of the projection then fits a float32 mantissa, and with
+    power-of-two level sizes so does reference + offset / size.
     """
     levels = tuple((int(h), int(w)) for h, w in levels)
     N_l = len(levels)
     S = N_l * N_p
     rng = np.random.default_rng(seed)
-    out = {
-        "query": rng.standard_normal((B, N_q, D)).astype(np.float32),
-        "reference_points": rng.uniform(0.0, 1.0, size=(B, N_q, N_l, 2)).astype(np.float32),
-        "offset_weight": (rng.standard_normal((N_h * S * 2, D)) * (offset_pixels / np.sqrt(D))).astype(np.float32),
-        "offset_bias": rng.normal(0.0, offset_pixels, size=N_h * S * 2).astype(np.float32),
-        "attention_weight": (rng.standard_normal((N_h * S, D)) / np.sqrt(D)).astype(np.float32),
-        "attention_bias": rng.normal(0.0, 0.1, size=N_h * S).astype(np.float32),
-    }
+    if dyadic:
+        out = {
+            "query": rng.integers(-2, 3, size=(B, N_q, D)).astype(np.float32),
+            "reference_points": (rng.integers(0, 257, size=(B, N_q, N_l, 2)) / 256.0).astype(np.float32),
+            "offset_weight": (rng.integers(-4, 5, size=(N_h * S * 2, D)) / 64.0).astype(np.float32),
+            "offset_bias": (rng.integers(-64, 65, size=N_h * S * 2) / 64.0).astype(np.float32),
+            "attention_weight": (rng.integers(-4, 5, size=(N_h * S, D)) / 256.0).astype(np.float32),
+            "attention_bias": (rng.integers(-16, 17, size=N_h * S) / 64.0).astype(np.float32),
+        }
+    else:
+        out = {
+            "query": rng.standard_normal((B, N_q, D)).astype(np.float32),
+            "reference_points": rng.uniform(0.0, 1.0, size=(B, N_q, N_l, 2)).astype(np.float32),
+            "offset_weight": (rng.standard_normal((N_h * S * 2, D)) * (offset_pixels / np.sqrt(D))).astype(np.float32),
+            "offset_bias": rng.normal(0.0, offset_pixels, size=N_h * S * 2).astype(np.float32),
+            "attention_weight": (rng.standard_normal((N_h * S, D)) / np.sqrt(D)).astype(np.float32),
+            "attention_bias": rng.normal(0.0, 0.1, size=N_h * S).astype(np.float32),
+        }
     if value_dtype == "bf16":
         for k in ("query", "offset_weight", "attention_weight"):
             bits = bf16_round_bits(out[k])

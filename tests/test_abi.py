@@ -35,7 +35,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == binding.ABI_VERSION == 2
+    assert lib.msda_abi_version() == binding.ABI_VERSION == 3
     for code, name in binding.STATUS_NAMES.items():
         assert lib.msda_status_string(code).decode().startswith(name)
     assert lib.msda_status_string(99) is not None
@@ -207,3 +207,90 @@ def test_python_binding_rejects_cpu_tensors(lib):
     a = torch.zeros(1, 5, 2, 2, 2)
     with pytest.raises(ValueError):
         binding.msda_forward(v, LEVELS, STARTS, loc, a)
+
+
+# ---------------------------------------------------------------- producer ---
+
+Q = {k: ctypes.c_void_p(0x20_0000_0000 + i * 0x1_0000_0000) for i, k in
+     enumerate(["query", "ref", "w_off", "b_off", "w_att", "b_att", "loc", "attn", "value", "out",
+                "gq", "gref", "gwo", "gbo", "gwa", "gba", "gloc", "gattn", "ws"])}
+D_FEAT = 16
+
+
+def _pfwd(lib, prob, D=D_FEAT, **over):
+    a = {k: Q[k] for k in ("query", "ref", "w_off", "b_off", "w_att", "b_att", "loc", "attn")}
+    a.update(over)
+    return lib.msda_producer_forward(ctypes.byref(prob), D, a["query"], a["ref"], a["w_off"], a["b_off"],
+                                     a["w_att"], a["b_att"], a["loc"], a["attn"], None)
+
+
+def _pfused(lib, prob, D=D_FEAT, **over):
+    a = {k: Q[k] for k in ("query", "ref", "w_off", "b_off", "w_att", "b_att", "value", "out", "loc",
+                           "attn")}
+    a.update(over)
+    return lib.msda_fused_forward(ctypes.byref(prob), D, a["query"], a["ref"], a["w_off"], a["b_off"],
+                                  a["w_att"], a["b_att"], a["value"], a["out"], a["loc"], a["attn"], None)
+
+
+def _pbwd(lib, prob, D=D_FEAT, ws_bytes=1 << 30, **over):
+    a = {k: Q[k] for k in ("query", "w_off", "w_att", "attn", "gloc", "gattn", "gq", "gref", "gwo", "gbo",
+                           "gwa", "gba", "ws")}
+    a.update(over)
+    return lib.msda_producer_backward(ctypes.byref(prob), D, a["query"], a["w_off"], a["w_att"], a["attn"],
+                                      a["gloc"], a["gattn"], a["gq"], a["gref"], a["gwo"], a["gbo"], a["gwa"],
+                                      a["gba"], a["ws"], ws_bytes, None)
+
+
+def test_producer_rejects_bad_arguments(lib):
+    prob, keep = _prob()
+    assert lib.msda_producer_forward(None, D_FEAT, *[None] * 8, None) == 1
+    assert _pfwd(lib, prob, D=0) == 1
+    assert _pfwd(lib, prob, query=None) == 1
+    assert _pfwd(lib, prob, loc=None) == 1
+    assert _pfwd(lib, prob, ref=ctypes.c_void_p(Q["ref"].value + 2)) == 1
+    assert _pfwd(lib, prob, attn=ctypes.c_void_p(Q["query"].value + 64)) == 1   # output over an input
+    assert _pfused(lib, prob, value=None) == 1
+    assert _pfused(lib, prob, out=ctypes.c_void_p(Q["value"].value + 16)) == 1
+    assert _pfused(lib, prob, loc=ctypes.c_void_p(Q["out"].value + 16)) == 1
+
+
+def test_producer_sample_limits(lib):
+    # N_l * N_p = 2 * 33 = 66 > 64 for the producer; 2 * 17 = 34 > 32 for the fused kernel
+    prob, keep = _prob(N_p=33)
+    assert _pfwd(lib, prob) == 4
+    prob, keep = _prob(N_p=17)
+    assert _pfused(lib, prob) == 4
+    assert _pfwd(lib, prob) != 4
+
+
+def test_producer_empty_problem_is_noop(lib):
+    prob, keep = _prob(N_q=0)
+    assert _pfwd(lib, prob, query=None, ref=None, w_off=None, w_att=None, loc=None, attn=None) == 0
+    assert _pfused(lib, prob, query=None, value=None, out=None) == 0
+    # no rows and no weight gradient asked for: nothing to enqueue
+    assert _pbwd(lib, prob, gwo=None, gbo=None, gwa=None, gba=None, query=None, attn=None) == 0
+
+
+def test_producer_backward_validation(lib):
+    prob, keep = _prob()
+    assert _pbwd(lib, prob, gq=None, gref=None, gwo=None, gbo=None, gwa=None, gba=None) == 3
+    assert _pbwd(lib, prob, ws_bytes=16) == 5
+    assert _pbwd(lib, prob, ws=None) == 5
+    assert _pbwd(lib, prob, gq=ctypes.c_void_p(Q["query"].value + 4)) == 1
+    assert _pbwd(lib, prob, gwa=ctypes.c_void_p(Q["gwo"].value + 4)) == 1
+    assert _pbwd(lib, prob, ws=ctypes.c_void_p(Q["ws"].value + 8)) == 1
+    assert _pbwd(lib, prob, attn=None) == 1
+
+
+def test_producer_workspace_size(lib):
+    # encoder shape, D = 256: row chunks x heads x 3S projection outputs x (D + 1) floats
+    levels = ((100, 167), (50, 84), (25, 42), (13, 21))
+    starts = (0, 16700, 20900, 21950)
+    prob, keep = binding.make_problem(2, 22223, 22223, 8, 32, levels, starts, 4)
+    sz = ctypes.c_size_t(0)
+    assert lib.msda_producer_backward_workspace_size(ctypes.byref(prob), 256, ctypes.byref(sz)) == 0
+    M = 2 * 22223
+    per_chunk = 8 * 48 * 257 * 4
+    assert sz.value % per_chunk == 0
+    chunks = sz.value // per_chunk
+    assert 16 <= chunks <= 64 and chunks * 32 >= M // 64

@@ -107,3 +107,14 @@ def test_backward_matches_finite_differences(layout):
             p_lo[name][idx] -= eps
             fd = (loss(p_hi) - loss(p_lo)) / (2 * eps)
             assert abs(fd - g[name][idx]) <= 1e-6 * (1 + abs(fd)), (name, idx, fd, g[name][idx])
+
+
+def test_dyadic_inputs_give_float32_exact_locations():
+    """The dyadic draw with power-of-two levels makes every location a float32
+    number exactly (the fused kernel's exact-location parity case relies on it)."""
+    levels = ((16, 16), (8, 8), (4, 4))
+    d = make_producer_inputs(2, levels, 40, 2, 3, 64, 11, dyadic=True)
+    loc, attn = producer.forward(d["query"], d["reference_points"], d["offset_weight"], d["offset_bias"],
+                                 d["attention_weight"], d["attention_bias"], levels, 2, 3)
+    np.testing.assert_array_equal(loc, loc.astype(np.float32).astype(np.float64))
+    assert np.abs(loc).max() < 2.0 and np.isfinite(attn).all()
