@@ -305,7 +305,8 @@ msda_status check_producer(const msda_problem* p, int64_t D, bool fused, Geometr
     pg->Nl = g->Nl;
     pg->Np = g->Np;
     pg->Nq = g->Nq;
-    pg->ct = (int32_t)((3 * S + 15) / 16);
+    const int64_t ct = (3 * S + 15) / 16;
+    pg->ct = ct <= 3 ? 3 : ct <= 6 ? 6 : 12;  // the instantiated column-tile counts
     pg->tpr = std::max(4, 1 << ilog2((int)S));
     pg->b2q = g->b2q;
     pg->loc_pair_aligned = 0;

@@ -19,7 +19,8 @@ struct ProducerGeom {
     int32_t D;                // features per query
     int32_t S;                // N_l * N_p
     int32_t Nh, Nl, Np, Nq;
-    int32_t ct;               // ceil(3 * S / 16) MFMA column tiles per head
+    int32_t ct;               // MFMA column tiles per head: 3, 6 or 12, the first >= 3 * S / 16
+                              // (tiles past the head's 3S columns compute zeros)
     int32_t tpr;              // lanes per (row, head) in the epilogues: power of two >= max(S, 4), <= 64
     int32_t b2q;              // locations in (B, 2, N_q, N_h, N_l, N_p)
     int32_t loc_pair_aligned; // BQHLP2 (x, y) pairs may be stored as one float2

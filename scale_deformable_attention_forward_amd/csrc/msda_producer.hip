@@ -56,31 +56,95 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Stage columns [k0, k0 + KC) of `nrows` rows of a row-major operand into
-// dst (row stride `dst_stride` floats) as float32. row_ptr(r) gives the start
-// of row r, or nullptr for a zero row; columns at or past `ncols` are zero.
-// vec == 4: the row starts are aligned for 4-element loads and ncols % 4 == 0.
-template <int KC, typename TQ, typename RowFn>
-__device__ __forceinline__ void stage_rows(float* dst, int dst_stride, int nrows, int k0, int ncols, int vec,
-                                           RowFn row_ptr)
+// Per-(row, sample) loops run tpr lanes per row and kBlock / tpr rows per
+// pass; a tile of kPRows rows takes at most this many passes (tpr <= 16, 32,
+// 64 for 3, 6, 12 column tiles).
+template <int CTM>
+constexpr int max_passes()
 {
+    return 4 * CTM / 3;
+}
+
+// Four consecutive elements of an operand row, as loaded from memory.
+template <typename TQ> struct Quad;
+template <> struct Quad<float> {
+    float4 v;
+};
+template <> struct Quad<uint16_t> {
+    uint2 v;
+};
+
+__device__ __forceinline__ float4 to_float4(const Quad<float>& q) { return q.v; }
+__device__ __forceinline__ float4 to_float4(const Quad<uint16_t>& q)
+{
+    return make_float4(__uint_as_float(q.v.x << 16), __uint_as_float(q.v.x & 0xffff0000u),
+                       __uint_as_float(q.v.y << 16), __uint_as_float(q.v.y & 0xffff0000u));
+}
+
+// Elements c..c+3 of `row` (nullptr: a zero row); columns at or past ncols
+// read 0. vec == 4: one vector load (row + c aligned, ncols % 4 == 0).
+__device__ __forceinline__ Quad<float> load_quad(const float* row, int c, int ncols, int vec)
+{
+    Quad<float> q{make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (!row || c >= ncols) return q;
     if (vec == 4) {
-        constexpr int per_row = KC / 4;
-        for (int e = threadIdx.x; e < nrows * per_row; e += kBlock) {
-            const int r = e / per_row, c = (e - r * per_row) * 4;
-            const TQ* p = row_ptr(r);
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p && k0 + c < ncols) VecIO<TQ, 4>::load(p + k0 + c, v);
-            *reinterpret_cast<float4*>(dst + r * dst_stride + c) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+        q.v = *reinterpret_cast<const float4*>(row + c);
     } else {
-        for (int e = threadIdx.x; e < nrows * KC; e += kBlock) {
-            const int r = e / KC, c = e - r * KC;
-            const TQ* p = row_ptr(r);
-            dst[r * dst_stride + c] = (p && k0 + c < ncols) ? load_f32(p + k0 + c) : 0.f;
+        q.v.x = row[c];
+        if (c + 1 < ncols) q.v.y = row[c + 1];
+        if (c + 2 < ncols) q.v.z = row[c + 2];
+        if (c + 3 < ncols) q.v.w = row[c + 3];
+    }
+    return q;
+}
+
+__device__ __forceinline__ Quad<uint16_t> load_quad(const uint16_t* row, int c, int ncols, int vec)
+{
+    Quad<uint16_t> q{make_uint2(0u, 0u)};
+    if (!row || c >= ncols) return q;
+    if (vec == 4) {
+        q.v = *reinterpret_cast<const uint2*>(row + c);
+    } else {
+        uint32_t e[4] = {row[c], 0u, 0u, 0u};
+        if (c + 1 < ncols) e[1] = row[c + 1];
+        if (c + 2 < ncols) e[2] = row[c + 2];
+        if (c + 3 < ncols) e[3] = row[c + 3];
+        q.v = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+    return q;
+}
+
+// A tile of rows x (4 * PR) columns of a row-major operand held in
+// registers: quad i of a thread is element e = threadIdx.x + i * kBlock of the
+// tile, row e / PR, columns 4 * (e % PR) .. + 3. load() issues every load
+// before any is used, so a tile costs one memory round trip; store() writes
+// it to LDS as float32.
+template <typename TQ, int NQ, int PR>
+struct TileRegs {
+    Quad<TQ> q[NQ];
+
+    // row_ptr(r): start of row r or nullptr (zero row); columns k0.. of the rows
+    template <typename RowFn>
+    __device__ __forceinline__ void load(int nrows, int k0, int ncols, int vec, RowFn row_ptr)
+    {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = threadIdx.x + i * kBlock;
+            const int r = e / PR, c = k0 + (e - r * PR) * 4;
+            q[i] = load_quad(r < nrows ? row_ptr(r) : nullptr, c, ncols, vec);
         }
     }
-}
+
+    __device__ __forceinline__ void store(float* dst, int stride, int nrows) const
+    {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = threadIdx.x + i * kBlock;
+            const int r = e / PR, c = (e - r * PR) * 4;
+            if (r < nrows) *reinterpret_cast<float4*>(dst + r * stride + c) = to_float4(q[i]);
+        }
+    }
+};
 
 // Row j of head h's projection matrix: the 2S offset rows, then the S logit rows.
 template <typename TQ>
@@ -94,48 +158,57 @@ __device__ __forceinline__ const TQ* head_weight_row(const ProducerGeom& pg, con
 
 // acc[t] = rows 16w..16w+15 (w = this wave) of the 64-row query tile starting
 // at row m0 (rows at or past `rows_valid` read as zero) times column tile t of
-// head h, summed over the D features in steps of kPKc. s_x holds kPRows and
-// s_w holds 16 * ct rows of kPStride floats.
-template <typename TQ>
+// head h, summed over the D features kPKc at a time. The next step's operands
+// are loaded into registers while the matrix cores work on the current one.
+// s_x holds kPRows and s_w 16 * ct rows of kPStride floats.
+template <typename TQ, int CTM>
 __device__ __forceinline__ void head_projection(const ProducerGeom& pg, const ProducerArgs<TQ>& a, int m0,
-                                                int rows_valid, int h, float* s_x, float* s_w,
-                                                f32x4 (&acc)[kPMaxColTiles])
+                                                int rows_valid, int h, float* s_x, float* s_w, f32x4 (&acc)[CTM])
 {
+    constexpr int PR = kPKc / 4;
+    constexpr int XQ = kPRows * PR / kBlock;
+    constexpr int WQ = (16 * CTM * PR + kBlock - 1) / kBlock;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    constexpr int wrows = 16 * CTM;
+    auto xrow = [&](int r) -> const TQ* { return r < rows_valid ? a.query + (size_t)(m0 + r) * pg.D : nullptr; };
+    auto wrow = [&](int j) -> const TQ* { return head_weight_row(pg, a, h, j); };
+    TileRegs<TQ, XQ, PR> xr;
+    TileRegs<TQ, WQ, PR> wr;
+    xr.load(kPRows, 0, pg.D, pg.vec, xrow);
+    wr.load(wrows, 0, pg.D, pg.vec, wrow);
 #pragma unroll
-    for (int t = 0; t < kPMaxColTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CTM; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* xa = s_x + (16 * wave + (lane & 15)) * kPStride + (lane >> 4);
+    const float* wb = s_w + (lane & 15) * kPStride + (lane >> 4);
     for (int k0 = 0; k0 < pg.D; k0 += kPKc) {
         __syncthreads();  // the previous step's tiles are consumed
-        stage_rows<kPKc, TQ>(s_x, kPStride, kPRows, k0, pg.D, pg.vec, [&](int r) -> const TQ* {
-            return r < rows_valid ? a.query + (size_t)(m0 + r) * pg.D : nullptr;
-        });
-        stage_rows<kPKc, TQ>(s_w, kPStride, 16 * pg.ct, k0, pg.D, pg.vec,
-                             [&](int j) -> const TQ* { return head_weight_row(pg, a, h, j); });
+        xr.store(s_x, kPStride, kPRows);
+        wr.store(s_w, kPStride, wrows);
         __syncthreads();
-        const float* xa = s_x + (16 * wave + (lane & 15)) * kPStride + (lane >> 4);
-        const float* wb = s_w + (lane & 15) * kPStride + (lane >> 4);
+        if (k0 + kPKc < pg.D) {
+            xr.load(kPRows, k0 + kPKc, pg.D, pg.vec, xrow);
+            wr.load(wrows, k0 + kPKc, pg.D, pg.vec, wrow);
+        }
 #pragma unroll
         for (int kk = 0; kk < kPKc; kk += 4) {
             const float av = xa[kk];
 #pragma unroll
-            for (int t = 0; t < kPMaxColTiles; ++t)
-                if (t < pg.ct) acc[t] = mfma_16x16x4(av, wb[t * 16 * kPStride + kk], acc[t]);
+            for (int t = 0; t < CTM; ++t) acc[t] = mfma_16x16x4(av, wb[t * 16 * kPStride + kk], acc[t]);
         }
     }
 }
 
 // Write the projection tile into s_o (kPRows rows of `ost` floats): MFMA
 // output element v of lane l is row 4 * (l / 16) + v, column l % 16 of its tile.
-__device__ __forceinline__ void store_projection(const ProducerGeom& pg, const f32x4 (&acc)[kPMaxColTiles], float* s_o,
-                                                 int ost)
+template <int CTM>
+__device__ __forceinline__ void store_projection(const ProducerGeom& pg, const f32x4 (&acc)[CTM], float* s_o, int ost)
 {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     float* o = s_o + (16 * wave + 4 * (lane >> 4)) * ost + (lane & 15);
 #pragma unroll
-    for (int t = 0; t < kPMaxColTiles; ++t)
-        if (t < pg.ct)
+    for (int t = 0; t < CTM; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o[v * ost + 16 * t] = acc[t][v];
+        for (int v = 0; v < 4; ++v) o[v * ost + 16 * t] = acc[t][v];
 }
 
 // Epilogue of one head over the 64-row tile in s_o: for row r and sample j,
@@ -143,35 +216,64 @@ __device__ __forceinline__ void store_projection(const ProducerGeom& pg, const f
 // weight (softmax over the head's S logits). tpr lanes per row (tpr >= S, a
 // power of two, 4..64), lane j < S holds sample j; rows at or past rows_valid
 // are not emitted. ref_rows points at the reference points of row m0.
-template <typename Emit>
-__device__ __forceinline__ void head_outputs(const Geometry& g, const ProducerGeom& pg, const float* s_o, int ost,
-                                             const float* b_off, const float* b_att, const float* ref_rows,
-                                             int rows_valid, int h, Emit emit)
-{
-    const int S = pg.S, tpr = pg.tpr;
-    const int rpp = kBlock / tpr;
-    const int j = threadIdx.x & (tpr - 1);
-    const bool jok = j < S;
-    for (int r0 = 0; r0 < kPRows; r0 += rpp) {
-        const int r = r0 + (int)threadIdx.x / tpr;
-        const float* o = s_o + r * ost;
-        const float z = jok ? o[2 * S + j] + (b_att ? b_att[h * S + j] : 0.f) : -INFINITY;
-        float mx = z;
-        for (int d = tpr >> 1; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
-        const float e = jok ? expf(z - mx) : 0.f;
-        float sum = e;
-        for (int d = tpr >> 1; d > 0; d >>= 1) sum += __shfl_xor(sum, d, kWave);
-        if (jok && r < rows_valid) {
-            const int l = j / pg.Np;
-            int H, W, start;
-            level_of(g.lv, l, H, W, start);
-            const float ox = o[2 * j] + (b_off ? b_off[h * 2 * S + 2 * j] : 0.f);
-            const float oy = o[2 * j + 1] + (b_off ? b_off[h * 2 * S + 2 * j + 1] : 0.f);
-            const float* rp = ref_rows + (r * pg.Nl + l) * 2;
-            emit(r, j, l, rp[0] + ox / (float)W, rp[1] + oy / (float)H, e / sum);
+// Two phases: HeadOut::load copies the thread's projection outputs (and its
+// biases and reference points) into registers, so the caller may reuse the
+// LDS of s_o after a barrier; HeadOut::finish computes and emits.
+template <int CTM>
+struct HeadOut {
+    static constexpr int PMAX = max_passes<CTM>();
+    float ox[PMAX], oy[PMAX], oz[PMAX], rx[PMAX], ry[PMAX];
+    int l, W, H;
+
+    __device__ __forceinline__ void load(const Geometry& g, const ProducerGeom& pg, const float* s_o, int ost,
+                                         const float* b_off, const float* b_att, const float* ref_rows,
+                                         int rows_valid, int h)
+    {
+        const int S = pg.S, tpr = pg.tpr;
+        const int rpp = kBlock / tpr, passes = kPRows / rpp;
+        const int j = threadIdx.x & (tpr - 1), r_in = (int)threadIdx.x / tpr;
+        const bool jok = j < S;
+        l = jok ? j / pg.Np : 0;
+        int start;
+        level_of(g.lv, l, H, W, start);
+        const float bx = jok && b_off ? b_off[h * 2 * S + 2 * j] : 0.f;
+        const float by = jok && b_off ? b_off[h * 2 * S + 2 * j + 1] : 0.f;
+        const float bz = jok && b_att ? b_att[h * S + j] : 0.f;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            const int r = p * rpp + r_in;
+            const bool ok = p < passes && jok && r < rows_valid;
+            rx[p] = ok ? ref_rows[(r * pg.Nl + l) * 2] : 0.f;
+            ry[p] = ok ? ref_rows[(r * pg.Nl + l) * 2 + 1] : 0.f;
+            const float* o = s_o + min(r, kPRows - 1) * ost;
+            ox[p] = p < passes && jok ? o[2 * j] + bx : 0.f;
+            oy[p] = p < passes && jok ? o[2 * j + 1] + by : 0.f;
+            oz[p] = p < passes && jok ? o[2 * S + j] + bz : -INFINITY;
         }
     }
-}
+
+    template <typename Emit>
+    __device__ __forceinline__ void finish(const ProducerGeom& pg, int rows_valid, Emit emit) const
+    {
+        const int S = pg.S, tpr = pg.tpr;
+        const int rpp = kBlock / tpr, passes = kPRows / rpp;
+        const int j = threadIdx.x & (tpr - 1), r_in = (int)threadIdx.x / tpr;
+        const bool jok = j < S;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p < passes) {  // uniform
+                const int r = p * rpp + r_in;
+                float mx = oz[p];
+                for (int d = tpr >> 1; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+                const float e = jok ? expf(oz[p] - mx) : 0.f;
+                float sum = e;
+                for (int d = tpr >> 1; d > 0; d >>= 1) sum += __shfl_xor(sum, d, kWave);
+                if (jok && r < rows_valid)
+                    emit(r, j, l, rx[p] + ox[p] / (float)W, ry[p] + oy[p] / (float)H, e / sum);
+            }
+        }
+    }
+};
 
 // Store one sample's location (in the requested layout) and weight.
 __device__ __forceinline__ void store_sample(const ProducerGeom& pg, int m, int h, int j, float ux, float uy, float A,
@@ -194,15 +296,6 @@ __device__ __forceinline__ void store_sample(const ProducerGeom& pg, int m, int 
     }
 }
 
-// Row tile and head of a producer workgroup: heads fastest, so the N_h
-// workgroups of one row tile run back to back on one XCD and share its L2.
-__device__ __forceinline__ void producer_tile(const ProducerGeom& pg, int& m0, int& h)
-{
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    h = lb % pg.Nh;
-    m0 = (lb / pg.Nh) * kPRows;
-}
-
 // Dynamic LDS floats of the projection phase: the staged K tiles, later the
 // output tile (aliased).
 __host__ __device__ inline int projection_lds_floats(int ct)
@@ -212,7 +305,9 @@ __host__ __device__ inline int projection_lds_floats(int ct)
     return stage > out ? stage : out;
 }
 
-template <typename TQ>
+// Grid: row tiles x heads with heads fastest, so the N_h workgroups of one row
+// tile run back to back on one XCD and share its L2.
+template <typename TQ, int CTM>
 __global__ __launch_bounds__(kBlock) void producer_forward_kernel(Geometry g, ProducerGeom pg, ProducerArgs<TQ> a,
                                                                   float* __restrict__ loc, float* __restrict__ attn)
 {
@@ -220,27 +315,29 @@ __global__ __launch_bounds__(kBlock) void producer_forward_kernel(Geometry g, Pr
     float* s_x = reinterpret_cast<float*>(smem4);
     float* s_w = s_x + kPRows * kPStride;
     float* s_o = s_x;  // aliases the staging tiles once the K loop is done
-    const int ost = 16 * pg.ct + 4;
-    int m0, h;
-    producer_tile(pg, m0, h);
+    constexpr int ost = 16 * CTM + 4;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int h = lb % pg.Nh, m0 = (lb / pg.Nh) * kPRows;
     const int rows_valid = min(kPRows, pg.M - m0);
-    f32x4 acc[kPMaxColTiles];
-    head_projection(pg, a, m0, rows_valid, h, s_x, s_w, acc);
+    f32x4 acc[CTM];
+    head_projection<TQ, CTM>(pg, a, m0, rows_valid, h, s_x, s_w, acc);
     __syncthreads();  // every wave is done reading the staged tiles
-    store_projection(pg, acc, s_o, ost);
+    store_projection<CTM>(pg, acc, s_o, ost);
     __syncthreads();
-    head_outputs(g, pg, s_o, ost, a.b_off, a.b_att, a.ref + (size_t)m0 * pg.Nl * 2, rows_valid, h,
-                 [&](int r, int j, int, float ux, float uy, float A) {
-                     store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
-                 });
+    HeadOut<CTM> ho;
+    ho.load(g, pg, s_o, ost, a.b_off, a.b_att, a.ref + (size_t)m0 * pg.Nl * 2, rows_valid, h);
+    ho.finish(pg, rows_valid, [&](int r, int j, int, float ux, float uy, float A) {
+        store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
+    });
 }
 
 // Producer and forward sampler in one kernel. Workgroup = (b, h, 64
 // consecutive queries); workgroups of one (b, h) slab are consecutive and
 // each XCD sweeps a contiguous range of them (as in the sampler). Dynamic
-// LDS: the projection phase, then the gather records of the 64 queries
+// LDS: the projection phase, then (over the same bytes, once the epilogue
+// holds its inputs in registers) the gather records of the 64 queries
 // (float4 weights and FwdRecordPix, rows of S + 1 against bank conflicts).
-template <typename T, int VEC>
+template <typename T, int VEC, int CTM>
 __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, ProducerGeom pg, ProducerArgs<T> a,
                                                                const T* __restrict__ value, T* __restrict__ out,
                                                                float* __restrict__ loc, float* __restrict__ attn)
@@ -249,10 +346,10 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
     const int row = pg.S + 1;
     float4* s_rw = smem4;
     FwdRecordPix* s_rp = reinterpret_cast<FwdRecordPix*>(s_rw + kPRows * row);
-    float* s_x = reinterpret_cast<float*>(s_rp + kPRows * row);
+    float* s_x = reinterpret_cast<float*>(smem4);
     float* s_w = s_x + kPRows * kPStride;
     float* s_o = s_x;
-    const int ost = 16 * pg.ct + 4;
+    constexpr int ost = 16 * CTM + 4;
 
     const int qtiles = (g.Nq + kPRows - 1) / kPRows;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -262,22 +359,24 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
     const int m0 = b * g.Nq + q0;
     const int rows_valid = min(kPRows, g.Nq - q0);
 
-    f32x4 acc[kPMaxColTiles];
-    head_projection(pg, a, m0, rows_valid, h, s_x, s_w, acc);
+    f32x4 acc[CTM];
+    head_projection<T, CTM>(pg, a, m0, rows_valid, h, s_x, s_w, acc);
     __syncthreads();
-    store_projection(pg, acc, s_o, ost);
+    store_projection<CTM>(pg, acc, s_o, ost);
     __syncthreads();
-    head_outputs(g, pg, s_o, ost, a.b_off, a.b_att, a.ref + (size_t)m0 * pg.Nl * 2, rows_valid, h,
-                 [&](int r, int j, int l, float ux, float uy, float A) {
-                     if (loc || attn) store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
-                     int H, W, start;
-                     level_of(g.lv, l, H, W, start);
-                     float4 w;
-                     FwdRecordPix rp;
-                     sampler_record(g, ux, uy, A, H, W, start, w, rp);
-                     s_rw[r * row + j] = w;
-                     s_rp[r * row + j] = rp;
-                 });
+    HeadOut<CTM> ho;
+    ho.load(g, pg, s_o, ost, a.b_off, a.b_att, a.ref + (size_t)m0 * pg.Nl * 2, rows_valid, h);
+    __syncthreads();  // s_o is in registers: the records take its place
+    ho.finish(pg, rows_valid, [&](int r, int j, int l, float ux, float uy, float A) {
+        if (loc || attn) store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
+        int H, W, start;
+        level_of(g.lv, l, H, W, start);
+        float4 w;
+        FwdRecordPix rp;
+        sampler_record(g, ux, uy, A, H, W, start, w, rp);
+        s_rw[r * row + j] = w;
+        s_rp[r * row + j] = rp;
+    });
     __syncthreads();
 
     // gather: the sampler's lane layout (VEC channels per lane, 2^lpu_log2 lanes per unit)
@@ -301,52 +400,64 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
 // ---------------------------------------------------------------------------
 // Backward.
 
-// Loss gradients at the head's projection outputs for row m, sample j (lane j
-// of a group of tpr lanes; every lane of the group must call it): the offset
-// gradients gx, gy, the logit gradient gz, and the raw location gradients
-// (rawx, rawy). Rows that are not valid give zeros.
-__device__ __forceinline__ void head_grads(const Geometry& g, const ProducerGeom& pg, const ProducerGradIn& in,
-                                           int m, bool row_ok, int h, int j, float& gx, float& gy, float& gz,
-                                           float& rawx, float& rawy)
+// What one (row, sample) lane reads for the gradient at the head's
+// projection outputs: A, dL/dA and dL/dloc (x, y). Invalid lanes read zeros.
+struct GradIn {
+    float A, gA, lx, ly;
+};
+
+__device__ __forceinline__ GradIn load_grad_in(const ProducerGeom& pg, const ProducerGradIn& in, int m, bool ok, int h,
+                                               int j)
 {
+    GradIn r = {0.f, 0.f, 0.f, 0.f};
+    if (!ok) return r;
     const int S = pg.S;
-    const bool ok = row_ok && j < S;
     const int idx = (m * pg.Nh + h) * S + j;
-    const float A = ok ? in.attn[idx] : 0.f;
-    const float gA = ok && in.grad_attn ? in.grad_attn[idx] : 0.f;
-    float dot = A * gA;
-    for (int d = pg.tpr >> 1; d > 0; d >>= 1) dot += __shfl_xor(dot, d, kWave);
-    gz = A * (gA - dot);
-    rawx = rawy = 0.f;
-    if (ok && in.grad_loc) {
+    r.A = in.attn[idx];
+    if (in.grad_attn) r.gA = in.grad_attn[idx];
+    if (in.grad_loc) {
         if (pg.b2q) {
             const int b = m / pg.Nq, q = m - b * pg.Nq;
             const int plane = pg.Nq * pg.Nh * S;
             const int i = b * 2 * plane + (q * pg.Nh + h) * S + j;
-            rawx = in.grad_loc[i];
-            rawy = in.grad_loc[i + plane];
+            r.lx = in.grad_loc[i];
+            r.ly = in.grad_loc[i + plane];
         } else {
-            rawx = in.grad_loc[2 * idx];
-            rawy = in.grad_loc[2 * idx + 1];
+            r.lx = in.grad_loc[2 * idx];
+            r.ly = in.grad_loc[2 * idx + 1];
         }
     }
-    int H = 1, W = 1, start;
-    if (ok) level_of(g.lv, j / pg.Np, H, W, start);
-    gx = rawx / (float)W;
-    gy = rawy / (float)H;
+    return r;
 }
 
-// grad_query (MFMA: G tile x W) and grad_reference_points. Grid: row tiles x
-// column blocks of kPDBlock. Dynamic LDS: the head's gradient tile s_g
+// Gradients at the projection outputs from what load_grad_in read: offsets
+// gx = dL/dloc_x / W, gy = dL/dloc_y / H, logit gz = A (dL/dA - sum over the
+// head's samples of A dL/dA). Every lane of the tpr-lane group must call it
+// (the sum is a butterfly over the group). inv_w, inv_h: the lane's level size.
+__device__ __forceinline__ void finish_grads(const GradIn& r, int tpr, float W, float H, float& gx, float& gy, float& gz)
+{
+    float dot = r.A * r.gA;
+    for (int d = tpr >> 1; d > 0; d >>= 1) dot += __shfl_xor(dot, d, kWave);
+    gz = r.A * (r.gA - dot);
+    gx = r.lx / W;
+    gy = r.ly / H;
+}
+
+// grad_query (MFMA: gradient tile x W) and grad_reference_points. Grid: row
+// tiles x column blocks of kPDBlock. Dynamic LDS: the head's gradient tile s_g
 // (kPRows x gst), a 16-row slice of W (16 x kPWStride), and the location
-// gradient sums s_ref (kPRows x 2S).
-template <typename TQ>
+// gradient sums s_ref (kPRows x 2S). The next head's inputs and the next W
+// slice are loaded while the matrix cores work on the current ones.
+template <typename TQ, int CTM>
 __global__ __launch_bounds__(kBlock) void producer_bwd_rows_kernel(Geometry g, ProducerGeom pg, ProducerArgs<TQ> a,
                                                                    ProducerGradIn in, TQ* __restrict__ grad_query,
                                                                    float* __restrict__ grad_ref)
 {
+    constexpr int PMAX = max_passes<CTM>();
+    constexpr int PR = kPDBlock / 4;
+    constexpr int WQ = 16 * PR / kBlock;
     extern __shared__ float4 smem4[];
-    const int gst = 16 * pg.ct + 4;
+    constexpr int gst = 16 * CTM + 4;
     float* s_g = reinterpret_cast<float*>(smem4);
     float* s_wk = s_g + kPRows * gst;
     float* s_ref = s_wk + 16 * kPWStride;
@@ -357,48 +468,68 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_rows_kernel(Geometry g, P
     const int db = lb / nmt, m0 = (lb - db * nmt) * kPRows;
     const int d0 = db * kPDBlock;
     const int rows_valid = min(kPRows, pg.M - m0);
-    const int dtiles = min(16, (min(kPDBlock, pg.D - d0) + 15) / 16);
     const bool do_ref = grad_ref && db == 0;
+    const int tpr = pg.tpr, rpp = kBlock / tpr, passes = kPRows / rpp;
+    const int j = tid & (tpr - 1), r_in = tid / tpr;
+    const bool jok = j < S;
+    int H = 1, W = 1, start;
+    if (jok) level_of(g.lv, j / pg.Np, H, W, start);
 
     for (int i = tid; i < kPRows * gst; i += kBlock) s_g[i] = 0.f;  // padding columns stay zero
     f32x4 acc[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int tpr = pg.tpr, rpp = kBlock / tpr, j = tid & (tpr - 1);
+    GradIn gin[PMAX];
+    auto load_head = [&](int h) {
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            const int r = p * rpp + r_in;
+            gin[p] = load_grad_in(pg, in, m0 + r, p < passes && jok && r < rows_valid, h, j);
+        }
+    };
+    TileRegs<TQ, WQ, PR> wr;
+    auto load_slice = [&](int h, int kc) {
+        wr.load(16, d0, pg.D, pg.vec, [&](int i) -> const TQ* { return head_weight_row(pg, a, h, kc * 16 + i); });
+    };
+    load_head(0);
+    if (grad_query) load_slice(0, 0);
+    const float* ga = s_g + (16 * wave + (lane & 15)) * gst + (lane >> 4);
+    const float* wb = s_wk + (lane >> 4) * kPWStride + (lane & 15);
+
     for (int h = 0; h < pg.Nh; ++h) {
-        __syncthreads();  // s_g is free
-        for (int r0 = 0; r0 < kPRows; r0 += rpp) {
-            const int r = r0 + tid / tpr;
-            float gx, gy, gz, rx, ry;
-            head_grads(g, pg, in, m0 + r, r < rows_valid, h, j, gx, gy, gz, rx, ry);
-            if (j < S) {
+        __syncthreads();  // the previous head's gradient tile is consumed
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= passes) continue;  // uniform
+            const int r = p * rpp + r_in;
+            float gx, gy, gz;
+            finish_grads(gin[p], tpr, (float)W, (float)H, gx, gy, gz);
+            if (jok) {
                 s_g[r * gst + 2 * j] = gx;
                 s_g[r * gst + 2 * j + 1] = gy;
                 s_g[r * gst + 2 * S + j] = gz;
                 if (do_ref) {
                     // this thread owns (r, j) for every head: sums over h in order
                     float* sr = s_ref + r * 2 * S + 2 * j;
-                    sr[0] = h == 0 ? rx : sr[0] + rx;
-                    sr[1] = h == 0 ? ry : sr[1] + ry;
+                    sr[0] = h == 0 ? gin[p].lx : sr[0] + gin[p].lx;
+                    sr[1] = h == 0 ? gin[p].ly : sr[1] + gin[p].ly;
                 }
             }
         }
+        if (h + 1 < pg.Nh) load_head(h + 1);
         if (!grad_query) continue;
-        for (int kc = 0; kc < pg.ct; ++kc) {
-            __syncthreads();  // s_g written / previous W slice consumed
-            stage_rows<kPDBlock, TQ>(s_wk, kPWStride, 16, d0, pg.D, pg.vec, [&](int i) -> const TQ* {
-                return head_weight_row(pg, a, h, kc * 16 + i);
-            });
+        for (int kc = 0; kc < CTM; ++kc) {
+            __syncthreads();  // the gradient tile is written / the previous W slice consumed
+            wr.store(s_wk, kPWStride, 16);
             __syncthreads();
-            const float* ga = s_g + (16 * wave + (lane & 15)) * gst + kc * 16 + (lane >> 4);
-            const float* wb = s_wk + (lane >> 4) * kPWStride + (lane & 15);
+            if (kc + 1 < CTM) load_slice(h, kc + 1);
+            else if (h + 1 < pg.Nh) load_slice(h + 1, 0);
 #pragma unroll
             for (int kk = 0; kk < 16; kk += 4) {
-                const float av = ga[kk];
+                const float av = ga[kc * 16 + kk];
 #pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    if (t < dtiles) acc[t] = mfma_16x16x4(av, wb[kk * kPWStride + 16 * t], acc[t]);
+                for (int t = 0; t < 16; ++t) acc[t] = mfma_16x16x4(av, wb[kk * kPWStride + 16 * t], acc[t]);
             }
         }
     }
@@ -406,7 +537,7 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_rows_kernel(Geometry g, P
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int d = d0 + 16 * t + (lane & 15);
-            if (t >= dtiles || d >= pg.D) continue;
+            if (d >= pg.D) continue;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = m0 + 16 * wave + 4 * (lane >> 4) + v;
@@ -433,15 +564,19 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_rows_kernel(Geometry g, P
 // sum over the chunk's rows m of G[m, h, n] * x_m[d] (n over the head's 3S
 // projection outputs), part_b[chunk][h][n] = sum of G[m, h, n]. Grid:
 // (chunk, head, column block) with column blocks fastest. Dynamic LDS: G^T
-// (16 * ct rows x kPStride) and the query rows (kPKc x kPBStride).
-template <typename TQ>
+// (16 * ct rows x kPStride) and the query rows (kPKc x kPBStride). The next
+// step's inputs are loaded while the matrix cores work on the current ones.
+template <typename TQ, int CTM>
 __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g, ProducerGeom pg, ProducerArgs<TQ> a,
                                                                       ProducerGradIn in, float* __restrict__ part_w,
                                                                       float* __restrict__ part_b)
 {
+    constexpr int PMAX = max_passes<CTM>() / 2 > 0 ? max_passes<CTM>() / 2 : 1;  // passes over kPKc rows
+    constexpr int PR = kPWCols / 4;
+    constexpr int XQ = kPKc * PR / kBlock;
     extern __shared__ float4 smem4[];
     float* s_a = reinterpret_cast<float*>(smem4);
-    float* s_b = s_a + 16 * pg.ct * kPStride;
+    float* s_b = s_a + 16 * CTM * kPStride;
     const int S = pg.S, cols = 3 * S;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int ndb = (pg.D + kPWCols - 1) / kPWCols;
@@ -451,39 +586,55 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g
     const int mc = lb / (ndb * pg.Nh);
     const int d0 = db * kPWCols;
     const int mbeg = mc * pg.mrows, mend = min(pg.M, mbeg + pg.mrows);
+    const int tpr = pg.tpr, rpp = kBlock / tpr;
+    const int passes = rpp >= kPKc ? 1 : kPKc / rpp;
+    const int j = tid & (tpr - 1), r_in = tid / tpr;
+    const bool jok = j < S;
+    int H = 1, W = 1, start;
+    if (jok) level_of(g.lv, j / pg.Np, H, W, start);
 
-    for (int i = tid; i < 16 * pg.ct * kPStride; i += kBlock) s_a[i] = 0.f;  // padding rows stay zero
-    f32x4 acc[kPMaxColTiles];
+    for (int i = tid; i < 16 * CTM * kPStride; i += kBlock) s_a[i] = 0.f;  // padding rows stay zero
+    f32x4 acc[CTM];
 #pragma unroll
-    for (int t = 0; t < kPMaxColTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CTM; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float bsum = 0.f;
-    const int tpr = pg.tpr, rpp = kBlock / tpr, j = tid & (tpr - 1);
+
+    GradIn gin[PMAX];
+    TileRegs<TQ, XQ, PR> xr;
+    auto load_step = [&](int mm0) {
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            const int r = p * rpp + r_in;
+            gin[p] = load_grad_in(pg, in, mm0 + r, p < passes && jok && r < kPKc && mm0 + r < mend, h, j);
+        }
+        xr.load(kPKc, d0, pg.D, pg.vec,
+                [&](int r) -> const TQ* { return mm0 + r < mend ? a.query + (size_t)(mm0 + r) * pg.D : nullptr; });
+    };
+    load_step(mbeg);
+    const float* ab = s_a + (lane & 15) * kPStride + (lane >> 4);
+    const float* xb = s_b + (lane >> 4) * kPBStride + 16 * wave + (lane & 15);
     for (int mm0 = mbeg; mm0 < mend; mm0 += kPKc) {
         __syncthreads();  // previous step consumed
-        for (int r0 = 0; r0 < kPKc; r0 += rpp) {
-            // with rpp > kPKc the groups past the step's rows still join the shuffles
-            const int r = r0 + tid / tpr;
-            const bool in_step = r < kPKc;
-            float gx, gy, gz, rx, ry;
-            head_grads(g, pg, in, mm0 + r, in_step && mm0 + r < mend, h, j, gx, gy, gz, rx, ry);
-            if (in_step && j < S) {
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= passes) continue;  // uniform
+            const int r = p * rpp + r_in;
+            float gx, gy, gz;
+            finish_grads(gin[p], tpr, (float)W, (float)H, gx, gy, gz);
+            if (jok && r < kPKc) {
                 s_a[(2 * j) * kPStride + r] = gx;
                 s_a[(2 * j + 1) * kPStride + r] = gy;
                 s_a[(2 * S + j) * kPStride + r] = gz;
             }
         }
-        stage_rows<kPWCols, TQ>(s_b, kPBStride, kPKc, d0, pg.D, pg.vec, [&](int r) -> const TQ* {
-            return mm0 + r < mend ? a.query + (size_t)(mm0 + r) * pg.D : nullptr;
-        });
+        xr.store(s_b, kPBStride, kPKc);
         __syncthreads();
-        const float* ab = s_a + (lane & 15) * kPStride + (lane >> 4);
-        const float* xb = s_b + (lane >> 4) * kPBStride + 16 * wave + (lane & 15);
+        if (mm0 + kPKc < mend) load_step(mm0 + kPKc);
 #pragma unroll
         for (int kk = 0; kk < kPKc; kk += 4) {
             const float bv = xb[kk * kPBStride];
 #pragma unroll
-            for (int t = 0; t < kPMaxColTiles; ++t)
-                if (t < pg.ct) acc[t] = mfma_16x16x4(ab[t * 16 * kPStride + kk], bv, acc[t]);
+            for (int t = 0; t < CTM; ++t) acc[t] = mfma_16x16x4(ab[t * 16 * kPStride + kk], bv, acc[t]);
         }
         if (db == 0 && tid < cols) {
             const float* ar = s_a + tid * kPStride;
@@ -493,8 +644,7 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g
     const size_t base = ((size_t)mc * pg.Nh + h) * cols;
     const int d = d0 + 16 * wave + (lane & 15);
 #pragma unroll
-    for (int t = 0; t < kPMaxColTiles; ++t) {
-        if (t >= pg.ct) continue;
+    for (int t = 0; t < CTM; ++t) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int n = 16 * t + 4 * (lane >> 4) + v;
@@ -546,7 +696,8 @@ size_t producer_forward_lds(const ProducerGeom& pg) { return (size_t)projection_
 
 size_t fused_forward_lds(const ProducerGeom& pg)
 {
-    return (size_t)kPRows * (pg.S + 1) * (sizeof(float4) + sizeof(FwdRecordPix)) + producer_forward_lds(pg);
+    const size_t records = (size_t)kPRows * (pg.S + 1) * (sizeof(float4) + sizeof(FwdRecordPix));
+    return records > producer_forward_lds(pg) ? records : producer_forward_lds(pg);
 }
 
 size_t producer_bwd_rows_lds(const ProducerGeom& pg)
@@ -575,29 +726,46 @@ static ProducerArgs<TQ> typed(const ProducerArgsRaw& r)
                             static_cast<const TQ*>(r.w_att), r.b_att};
 }
 
+template <typename TQ, int CTM>
+static void launch_producer_forward_c(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, float* loc,
+                                      float* attn, hipStream_t stream)
+{
+    hipLaunchKernelGGL((producer_forward_kernel<TQ, CTM>), dim3(producer_row_tiles(pg.M) * pg.Nh), dim3(kBlock),
+                       producer_forward_lds(pg), stream, g, pg, typed<TQ>(a), loc, attn);
+}
+
+template <typename TQ>
+static void launch_producer_forward_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, float* loc,
+                                      float* attn, hipStream_t stream)
+{
+    switch (pg.ct) {
+    case 3: launch_producer_forward_c<TQ, 3>(g, pg, a, loc, attn, stream); break;
+    case 6: launch_producer_forward_c<TQ, 6>(g, pg, a, loc, attn, stream); break;
+    default: launch_producer_forward_c<TQ, 12>(g, pg, a, loc, attn, stream); break;
+    }
+}
+
 hipError_t launch_producer_forward(const Geometry& g, const ProducerGeom& pg, int bf16, const ProducerArgsRaw& a,
                                    float* loc, float* attn, hipStream_t stream)
 {
-    const dim3 grid(producer_row_tiles(pg.M) * pg.Nh);
-    const size_t lds = producer_forward_lds(pg);
-    if (bf16)
-        hipLaunchKernelGGL(producer_forward_kernel<uint16_t>, grid, dim3(kBlock), lds, stream, g, pg,
-                           typed<uint16_t>(a), loc, attn);
-    else
-        hipLaunchKernelGGL(producer_forward_kernel<float>, grid, dim3(kBlock), lds, stream, g, pg, typed<float>(a),
-                           loc, attn);
+    if (bf16) launch_producer_forward_t<uint16_t>(g, pg, a, loc, attn, stream);
+    else launch_producer_forward_t<float>(g, pg, a, loc, attn, stream);
     return hipGetLastError();
 }
 
 template <typename T, int VEC>
-static hipError_t launch_fused_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, const void* value,
-                                 void* out, float* loc, float* attn, hipStream_t stream)
+static void launch_fused_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, const void* value,
+                           void* out, float* loc, float* attn, hipStream_t stream)
 {
     const int qtiles = (g.Nq + kPRows - 1) / kPRows;
     const dim3 grid(g.B * g.Nh * qtiles);
-    hipLaunchKernelGGL((fused_forward_kernel<T, VEC>), grid, dim3(kBlock), fused_forward_lds(pg), stream, g, pg,
-                       typed<T>(a), static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
-    return hipGetLastError();
+    const size_t lds = fused_forward_lds(pg);
+    if (pg.ct == 3)
+        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, 3>), grid, dim3(kBlock), lds, stream, g, pg, typed<T>(a),
+                           static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
+    else
+        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, 6>), grid, dim3(kBlock), lds, stream, g, pg, typed<T>(a),
+                           static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
 }
 
 hipError_t launch_fused_forward(const Geometry& g, const ProducerGeom& pg, int bf16, int vec, const ProducerArgsRaw& a,
@@ -605,29 +773,31 @@ hipError_t launch_fused_forward(const Geometry& g, const ProducerGeom& pg, int b
 {
     if (bf16) {
         switch (vec) {
-        case 8: return launch_fused_t<uint16_t, 8>(g, pg, a, value, out, loc, attn, stream);
-        case 4: return launch_fused_t<uint16_t, 4>(g, pg, a, value, out, loc, attn, stream);
-        case 2: return launch_fused_t<uint16_t, 2>(g, pg, a, value, out, loc, attn, stream);
-        default: return launch_fused_t<uint16_t, 1>(g, pg, a, value, out, loc, attn, stream);
+        case 8: launch_fused_t<uint16_t, 8>(g, pg, a, value, out, loc, attn, stream); break;
+        case 4: launch_fused_t<uint16_t, 4>(g, pg, a, value, out, loc, attn, stream); break;
+        case 2: launch_fused_t<uint16_t, 2>(g, pg, a, value, out, loc, attn, stream); break;
+        default: launch_fused_t<uint16_t, 1>(g, pg, a, value, out, loc, attn, stream); break;
+        }
+    } else {
+        switch (vec) {
+        case 4: launch_fused_t<float, 4>(g, pg, a, value, out, loc, attn, stream); break;
+        case 2: launch_fused_t<float, 2>(g, pg, a, value, out, loc, attn, stream); break;
+        default: launch_fused_t<float, 1>(g, pg, a, value, out, loc, attn, stream); break;
         }
     }
-    switch (vec) {
-    case 4: return launch_fused_t<float, 4>(g, pg, a, value, out, loc, attn, stream);
-    case 2: return launch_fused_t<float, 2>(g, pg, a, value, out, loc, attn, stream);
-    default: return launch_fused_t<float, 1>(g, pg, a, value, out, loc, attn, stream);
-    }
+    return hipGetLastError();
 }
 
-template <typename TQ>
-static hipError_t launch_producer_backward_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& ar,
+template <typename TQ, int CTM>
+static hipError_t launch_producer_backward_c(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& ar,
                                              const ProducerGradIn& in, const ProducerGradOut& o, float* part,
                                              hipStream_t stream)
 {
     const ProducerArgs<TQ> a = typed<TQ>(ar);
     if (o.grad_query || o.grad_ref) {
         const dim3 grid(producer_row_tiles(pg.M) * producer_grad_query_blocks(pg.D));
-        hipLaunchKernelGGL(producer_bwd_rows_kernel<TQ>, grid, dim3(kBlock), producer_bwd_rows_lds(pg), stream, g, pg,
-                           a, in, static_cast<TQ*>(o.grad_query), o.grad_ref);
+        hipLaunchKernelGGL((producer_bwd_rows_kernel<TQ, CTM>), grid, dim3(kBlock), producer_bwd_rows_lds(pg), stream,
+                           g, pg, a, in, static_cast<TQ*>(o.grad_query), o.grad_ref);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -635,8 +805,8 @@ static hipError_t launch_producer_backward_t(const Geometry& g, const ProducerGe
         float* part_w = part;
         float* part_b = part + (size_t)pg.mchunks * pg.Nh * 3 * pg.S * pg.D;
         const dim3 grid(pg.mchunks * pg.Nh * producer_weight_col_blocks(pg.D));
-        hipLaunchKernelGGL(producer_bwd_weights_kernel<TQ>, grid, dim3(kBlock), producer_bwd_weights_lds(pg), stream,
-                           g, pg, a, in, part_w, part_b);
+        hipLaunchKernelGGL((producer_bwd_weights_kernel<TQ, CTM>), grid, dim3(kBlock), producer_bwd_weights_lds(pg),
+                           stream, g, pg, a, in, part_w, part_b);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int n = pg.Nh * 3 * pg.S * (pg.D + 1);
@@ -646,6 +816,18 @@ static hipError_t launch_producer_backward_t(const Geometry& g, const ProducerGe
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+template <typename TQ>
+static hipError_t launch_producer_backward_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a,
+                                             const ProducerGradIn& in, const ProducerGradOut& o, float* part,
+                                             hipStream_t stream)
+{
+    switch (pg.ct) {
+    case 3: return launch_producer_backward_c<TQ, 3>(g, pg, a, in, o, part, stream);
+    case 6: return launch_producer_backward_c<TQ, 6>(g, pg, a, in, o, part, stream);
+    default: return launch_producer_backward_c<TQ, 12>(g, pg, a, in, o, part, stream);
+    }
 }
 
 hipError_t launch_producer_backward(const Geometry& g, const ProducerGeom& pg, int bf16, const ProducerArgsRaw& a,
