@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense float32 matrix-core peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fp32_fwd_bwd_hbm_traffic.txt")
 METRIC = "queries/s and effective gathered HBM GB/s (% of peak), fwd+bwd, 1 MI355X"
 WORKLOAD_NUM = 5                # encoder shapes with grad_output (the forward uses the same arrays)
@@ -50,6 +51,9 @@ def parse():
                     help="also time steps with a 1 GiB scratch write before each launch (caches cold)")
     ap.add_argument("--report", action="store_true",
                     help="time every named workload (GPU warm/cold, CPU oracle all cores / 1 core)")
+    ap.add_argument("--producer", action="store_true",
+                    help="time the producer of locations and weights (projection + softmax), alone, fused "
+                         "with the sampler, and its backward, at the encoder shape with D=256")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
@@ -331,6 +335,102 @@ def report(a):
         print(json.dumps(line), flush=True)
 
 
+# --------------------------------------------------------------- producer ---
+
+def producer_workspace_bytes(binding, q, w, ss, ls):
+    import ctypes
+    lib = binding.load_library()
+    L = sum(h * wd for h, wd in ss)
+    prob, keep = binding.make_problem(w["B"], L, w["N_q"], w["N_h"], 1, ss, ls, w["N_p"], value_dtype=q.dtype)
+    n = ctypes.c_size_t(0)
+    assert lib.msda_producer_backward_workspace_size(ctypes.byref(prob), w["D"], ctypes.byref(n)) == 0
+    return max(1, n.value)
+
+
+def producer_report(a):
+    """One JSON line per input dtype: the producer forward, the fused producer
+    + sampler against the two-call chain, and the producer backward, with
+    FLOP/s against the float32 matrix-core peak, and the CPU oracle (float64
+    numpy) on a bounded slice of rows."""
+    import torch
+    import oracle.producer as oprod
+    from scale_deformable_attention_forward_amd import binding
+    from scale_deformable_attention_forward_amd.workloads import (PRODUCER_WORKLOAD, make_inputs,
+                                                                  make_producer_inputs)
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = PRODUCER_WORKLOAD
+    S = len(w["levels"]) * w["N_p"]
+    M = w["B"] * w["N_q"]
+    gemm_flop = 2.0 * M * 3 * w["N_h"] * S * w["D"]
+    for dtype in ("fp32", "bf16"):
+        p = make_producer_inputs(w["B"], w["levels"], w["N_q"], w["N_h"], w["N_p"], w["D"], w["seed"],
+                                 value_dtype=dtype, grad_seed=w["seed"] + 1)
+        v = make_inputs(w["B"], w["levels"], w["N_q"], w["N_h"], w["C_h"], w["N_p"], w["seed"] + 2,
+                        value_dtype=dtype)
+
+        def dev_t(k, src):
+            if dtype == "bf16" and k + "_bf16_bits" in src:
+                return torch.from_numpy(src[k + "_bf16_bits"].view(np.int16).copy()).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(src[k])).to(dev)
+
+        q, ref, wo, bo, wa, ba = (dev_t(k, p) for k in ("query", "reference_points", "offset_weight",
+                                                        "offset_bias", "attention_weight", "attention_bias"))
+        val = dev_t("value", v)
+        ss, ls = p["spatial_shapes"], p["level_start_index"]
+        loc, attn = binding.msda_producer_forward(q, ref, wo, bo, wa, ba, ss, ls, w["N_h"])
+        out = torch.empty((w["B"], w["N_q"], w["N_h"] * w["C_h"]), dtype=val.dtype, device=dev)
+        gl = dev_t("grad_sampling_locations", p)
+        ga = dev_t("grad_attention_weights", p)
+        grads = binding.msda_producer_backward(q, wo, wa, attn, gl, ga, ss, ls)   # outputs reused below
+        pws = torch.empty(producer_workspace_bytes(binding, q, w, ss, ls), dtype=torch.uint8, device=dev)
+        fns = {
+            "forward": lambda: binding.msda_producer_forward(q, ref, wo, bo, wa, ba, ss, ls, w["N_h"],
+                                                             sampling_locations=loc, attention_weights=attn,
+                                                             stream=stream),
+            "sampler": lambda: binding.msda_forward(val, ss, ls, loc, attn, output=out, stream=stream),
+            "fused_forward": lambda: binding.msda_fused_forward(val, ss, ls, q, ref, wo, bo, wa, ba,
+                                                                output=out, stream=stream),
+            "backward": lambda: binding.msda_producer_backward(q, wo, wa, attn, gl, ga, ss, ls, outputs=grads,
+                                                               workspace=pws, stream=stream),
+        }
+        ms = {k: time_launches(fn, stream, a.steps, a.warmup) for k, fn in fns.items()}
+        line = {"producer": f"encoder shape, D={w['D']}, {dtype} inputs", "B": w["B"], "N_q": w["N_q"],
+                "N_h": w["N_h"], "N_l": len(w["levels"]), "N_p": w["N_p"], "D": w["D"], "C_h": w["C_h"],
+                "flop_forward": gemm_flop, "flop_backward": 2 * gemm_flop,
+                "peak_tflops": MFMA_F32_PEAK_TFLOPS, "peak_note": "float32 matrix cores (bfloat16 inputs are "
+                                                                  "widened exactly and multiplied in float32)"}
+        for k, flop in (("forward", gemm_flop), ("fused_forward", None), ("backward", 2 * gemm_flop),
+                        ("sampler", None)):
+            r = stats(ms[k])
+            if flop:
+                tf = flop / (r["ms_mean"] * 1e-3) / 1e12
+                r.update(tflops=tf, frac_of_peak=tf / MFMA_F32_PEAK_TFLOPS)
+            r["queries_per_s"] = M / (r["ms_mean"] * 1e-3)
+            line[k] = r
+        line["fused_forward"]["two_call_chain_ms"] = line["forward"]["ms_mean"] + line["sampler"]["ms_mean"]
+        if not a.no_cpu_baseline:
+            rows = 2048
+            f64 = {k: p[k][:, :rows // w["B"]] for k in ("query", "reference_points")}
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < a.cpu_seconds / 4:
+                l64, a64 = oprod.forward(f64["query"], f64["reference_points"], p["offset_weight"],
+                                         p["offset_bias"], p["attention_weight"], p["attention_bias"],
+                                         ss, w["N_h"], w["N_p"])
+                oprod.backward(f64["query"], p["offset_weight"], p["attention_weight"], a64,
+                               p["grad_sampling_locations"][:, :rows // w["B"]],
+                               p["grad_attention_weights"][:, :rows // w["B"]], ss, w["N_h"], w["N_p"])
+                reps += 1
+            el = time.perf_counter() - t0
+            line["cpu_oracle"] = {"queries_per_s": reps * rows / el, "kind": "oracle",
+                                  "cores": len(os.sched_getaffinity(0)),
+                                  "sample": f"{reps} forward+backward passes over {rows} rows "
+                                            f"({el:.1f} s), float64 numpy (BLAS threads)"}
+        print(json.dumps(line), flush=True)
+
+
 # ------------------------------------------------------------------ main ---
 
 def main():
@@ -353,6 +453,9 @@ def main():
         return
     if a.report:
         report(a)
+        return
+    if a.producer:
+        producer_report(a)
         return
     from scale_deformable_attention_forward_amd import binding
     from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_workload

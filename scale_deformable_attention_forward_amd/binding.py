@@ -444,10 +444,11 @@ PRODUCER_GRADS = ("query", "reference_points", "offset_weight", "offset_bias", "
 def msda_producer_backward(query, offset_weight, attention_weight, attention_weights,
                            grad_sampling_locations, grad_attention_weights, spatial_shapes,
                            level_start_index, sampling_locations_layout="BQHLP2", compute=PRODUCER_GRADS,
-                           workspace=None, stream=None):
+                           workspace=None, outputs=None, stream=None):
     """Gradients of the producer's inputs (dict keyed by PRODUCER_GRADS; only
     the names in ``compute`` are computed, the others are None). Either output
-    gradient may be None (zero)."""
+    gradient may be None (zero). ``outputs`` may hold preallocated tensors for
+    any of the computed gradients."""
     lib = load_library()
     if attention_weights.dim() != 5:
         raise ValueError("attention_weights must have shape (B, N_q, N_h, N_l, N_p)")
@@ -475,8 +476,16 @@ def msda_producer_backward(query, offset_weight, attention_weight, attention_wei
               "offset_bias": ((N_h * N_l * N_p * 2,), torch.float32),
               "attention_weight": (attention_weight.shape, torch.float32),
               "attention_bias": ((N_h * N_l * N_p,), torch.float32)}
-    out = {k: (torch.empty(shapes[k][0], dtype=shapes[k][1], device=dev) if k in compute else None)
-           for k in PRODUCER_GRADS}
+    given = outputs or {}
+    out = {}
+    for k in PRODUCER_GRADS:
+        if k not in compute:
+            out[k] = None
+        elif given.get(k) is not None:
+            _check_optional(given[k], f"outputs[{k!r}]", shapes[k][0], shapes[k][1])
+            out[k] = given[k]
+        else:
+            out[k] = torch.empty(shapes[k][0], dtype=shapes[k][1], device=dev)
     L = sum(int(h) * int(w) for h, w in spatial_shapes)
     prob, keep = make_problem(B, L, N_q, N_h, 1, spatial_shapes, level_start_index, N_p, "BLNC",
                               sampling_locations_layout, False, "zeros", query.dtype)

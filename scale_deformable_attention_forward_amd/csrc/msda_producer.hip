@@ -49,6 +49,8 @@ constexpr int kPDBlock = 256;           // grad_query columns per workgroup (16 
 constexpr int kPWStride = kPDBlock + 16;
 constexpr int kPWCols = 64;             // weight-gradient columns per workgroup (one tile per wave)
 constexpr int kPBStride = kPWCols + 16;
+constexpr int kPMStep = 32;             // rows per step of the weight-gradient pass
+constexpr int kPMStride = kPMStep + 4;  // LDS row stride (floats) of its transposed gradient tile
 static_assert(kPRows == 4 * 16 && kBlock == 4 * kWave, "one 16-row MFMA tile per wave");
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c)
@@ -564,19 +566,19 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_rows_kernel(Geometry g, P
 // sum over the chunk's rows m of G[m, h, n] * x_m[d] (n over the head's 3S
 // projection outputs), part_b[chunk][h][n] = sum of G[m, h, n]. Grid:
 // (chunk, head, column block) with column blocks fastest. Dynamic LDS: G^T
-// (16 * ct rows x kPStride) and the query rows (kPKc x kPBStride). The next
+// (16 * ct rows x kPMStride) and the query rows (kPMStep x kPBStride). The next
 // step's inputs are loaded while the matrix cores work on the current ones.
 template <typename TQ, int CTM>
 __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g, ProducerGeom pg, ProducerArgs<TQ> a,
                                                                       ProducerGradIn in, float* __restrict__ part_w,
                                                                       float* __restrict__ part_b)
 {
-    constexpr int PMAX = max_passes<CTM>() / 2 > 0 ? max_passes<CTM>() / 2 : 1;  // passes over kPKc rows
+    constexpr int PMAX = max_passes<CTM>() / 2 > 0 ? max_passes<CTM>() / 2 : 1;  // passes over kPMStep rows
     constexpr int PR = kPWCols / 4;
-    constexpr int XQ = kPKc * PR / kBlock;
+    constexpr int XQ = kPMStep * PR / kBlock;
     extern __shared__ float4 smem4[];
     float* s_a = reinterpret_cast<float*>(smem4);
-    float* s_b = s_a + 16 * CTM * kPStride;
+    float* s_b = s_a + 16 * CTM * kPMStride;
     const int S = pg.S, cols = 3 * S;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int ndb = (pg.D + kPWCols - 1) / kPWCols;
@@ -587,13 +589,13 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g
     const int d0 = db * kPWCols;
     const int mbeg = mc * pg.mrows, mend = min(pg.M, mbeg + pg.mrows);
     const int tpr = pg.tpr, rpp = kBlock / tpr;
-    const int passes = rpp >= kPKc ? 1 : kPKc / rpp;
+    const int passes = rpp >= kPMStep ? 1 : kPMStep / rpp;
     const int j = tid & (tpr - 1), r_in = tid / tpr;
     const bool jok = j < S;
     int H = 1, W = 1, start;
     if (jok) level_of(g.lv, j / pg.Np, H, W, start);
 
-    for (int i = tid; i < 16 * CTM * kPStride; i += kBlock) s_a[i] = 0.f;  // padding rows stay zero
+    for (int i = tid; i < 16 * CTM * kPMStride; i += kBlock) s_a[i] = 0.f;  // padding rows stay zero
     f32x4 acc[CTM];
 #pragma unroll
     for (int t = 0; t < CTM; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -605,15 +607,15 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
             const int r = p * rpp + r_in;
-            gin[p] = load_grad_in(pg, in, mm0 + r, p < passes && jok && r < kPKc && mm0 + r < mend, h, j);
+            gin[p] = load_grad_in(pg, in, mm0 + r, p < passes && jok && r < kPMStep && mm0 + r < mend, h, j);
         }
-        xr.load(kPKc, d0, pg.D, pg.vec,
+        xr.load(kPMStep, d0, pg.D, pg.vec,
                 [&](int r) -> const TQ* { return mm0 + r < mend ? a.query + (size_t)(mm0 + r) * pg.D : nullptr; });
     };
     load_step(mbeg);
-    const float* ab = s_a + (lane & 15) * kPStride + (lane >> 4);
+    const float* ab = s_a + (lane & 15) * kPMStride + (lane >> 4);
     const float* xb = s_b + (lane >> 4) * kPBStride + 16 * wave + (lane & 15);
-    for (int mm0 = mbeg; mm0 < mend; mm0 += kPKc) {
+    for (int mm0 = mbeg; mm0 < mend; mm0 += kPMStep) {
         __syncthreads();  // previous step consumed
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
@@ -621,24 +623,24 @@ __global__ __launch_bounds__(kBlock) void producer_bwd_weights_kernel(Geometry g
             const int r = p * rpp + r_in;
             float gx, gy, gz;
             finish_grads(gin[p], tpr, (float)W, (float)H, gx, gy, gz);
-            if (jok && r < kPKc) {
-                s_a[(2 * j) * kPStride + r] = gx;
-                s_a[(2 * j + 1) * kPStride + r] = gy;
-                s_a[(2 * S + j) * kPStride + r] = gz;
+            if (jok && r < kPMStep) {
+                s_a[(2 * j) * kPMStride + r] = gx;
+                s_a[(2 * j + 1) * kPMStride + r] = gy;
+                s_a[(2 * S + j) * kPMStride + r] = gz;
             }
         }
-        xr.store(s_b, kPBStride, kPKc);
+        xr.store(s_b, kPBStride, kPMStep);
         __syncthreads();
-        if (mm0 + kPKc < mend) load_step(mm0 + kPKc);
+        if (mm0 + kPMStep < mend) load_step(mm0 + kPMStep);
 #pragma unroll
-        for (int kk = 0; kk < kPKc; kk += 4) {
+        for (int kk = 0; kk < kPMStep; kk += 4) {
             const float bv = xb[kk * kPBStride];
 #pragma unroll
-            for (int t = 0; t < CTM; ++t) acc[t] = mfma_16x16x4(ab[t * 16 * kPStride + kk], bv, acc[t]);
+            for (int t = 0; t < CTM; ++t) acc[t] = mfma_16x16x4(ab[t * 16 * kPMStride + kk], bv, acc[t]);
         }
         if (db == 0 && tid < cols) {
-            const float* ar = s_a + tid * kPStride;
-            for (int r = 0; r < kPKc; ++r) bsum += ar[r];
+            const float* ar = s_a + tid * kPMStride;
+            for (int r = 0; r < kPMStep; ++r) bsum += ar[r];
         }
     }
     const size_t base = ((size_t)mc * pg.Nh + h) * cols;
@@ -707,7 +709,7 @@ size_t producer_bwd_rows_lds(const ProducerGeom& pg)
 
 size_t producer_bwd_weights_lds(const ProducerGeom& pg)
 {
-    return ((size_t)16 * pg.ct * kPStride + (size_t)kPKc * kPBStride) * sizeof(float);
+    return ((size_t)16 * pg.ct * kPMStride + (size_t)kPMStep * kPBStride) * sizeof(float);
 }
 
 size_t producer_bwd_workspace_floats(const ProducerGeom& pg)

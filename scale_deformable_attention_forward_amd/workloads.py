@@ -82,6 +82,11 @@ WORKLOADS = {
 }
 
 
+# The producer of locations and weights at the encoder shape, with the
+# feature width of Deformable-DETR-style encoders (D = N_h * C_h = 256).
+PRODUCER_WORKLOAD = dict(B=2, levels=ENCODER_LEVELS, N_q=22223, N_h=8, N_p=4, C_h=32, D=256, seed=61)
+
+
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even float32 -> bfloat16, returned as uint16 bit patterns."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
