@@ -16,8 +16,8 @@
 #include "msda_producer.h"
 
 namespace msda {
-hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
-                          const float* attn, void* out, hipStream_t stream);
+hipError_t launch_forward(const Geometry& g, int bf16, int vec, int64_t value_bytes, const void* value,
+                          const float* loc, const float* attn, void* out, hipStream_t stream);
 hipError_t launch_zero_elems(void* p, int64_t n, int elem, hipStream_t stream);
 hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int bf16, int accumulate,
                                 const void* grad_out, const void* value, const float* loc, const float* attn,
@@ -368,8 +368,8 @@ msda_status msda_forward(const msda_problem* problem, const void* value, const f
     g.units = (int32_t)units;
     g.blocks = (int32_t)((units + upb - 1) / upb);
     g.loc_pair_aligned = aligned(sampling_locations, 8);
-    const hipError_t e = msda::launch_forward(g, problem->value_dtype == MSDA_BF16, vec, value,
-                                              sampling_locations, attention_weights, output, stream);
+    const hipError_t e = msda::launch_forward(g, problem->value_dtype == MSDA_BF16, vec, (int64_t)z.value_bytes,
+                                              value, sampling_locations, attention_weights, output, stream);
     return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
 }
 
@@ -541,8 +541,8 @@ msda_status msda_fused_forward(const msda_problem* problem, int64_t D, const voi
     pg.loc_pair_aligned = sampling_locations && aligned(sampling_locations, 8);
     const hipError_t e = msda::launch_fused_forward(
         g, pg, problem->value_dtype == MSDA_BF16, vec,
-        producer_args(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias), value,
-        output, sampling_locations, attention_weights, stream);
+        producer_args(query, reference_points, offset_weight, offset_bias, attention_weight, attention_bias),
+        (int64_t)z.value_bytes, value, output, sampling_locations, attention_weights, stream);
     return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
 }
 

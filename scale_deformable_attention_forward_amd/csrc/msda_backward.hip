@@ -43,8 +43,8 @@ namespace msda {
 struct BwdRecord {
     float fx, fy;   // fractional offsets inside the cell
     float kx, ky;   // d(pixel)/d(location) per axis, 0 where border clamped
-    int32_t pix;    // flat pixel index (along L) of corner (x0, y0)
-    int32_t W;      // level row length in pixels
+    int32_t off;    // element offset of corner (x0, y0) within the (b, h) slab of value
+    int32_t rowp;   // element distance between pixel rows of the level
     int32_t mask;   // bit k: corner k = 2*dy + dx lies inside the level
     float a;        // attention weight
 };
@@ -168,8 +168,9 @@ __device__ __forceinline__ BwdRecord make_record(const Geometry& g, float ux, fl
     r.fy = y - y0f;
     r.kx = kx;
     r.ky = ky;
-    r.pix = start + y0 * W + x0;
-    r.W = W;
+    const uint32_t pstride = (uint32_t)(g.bnlc ? g.Ch : g.Nh * g.Ch);  // element distance between neighbouring pixels
+    r.off = (int32_t)((uint32_t)(start + y0 * W + x0) * pstride);  // may wrap for corners outside the level (masked)
+    r.rowp = (int32_t)((uint32_t)W * pstride);
     r.mask = (ix0 && iy0 ? 1 : 0) | (ix1 && iy0 ? 2 : 0) | (ix0 && iy1 ? 4 : 0) | (ix1 && iy1 ? 8 : 0);
     r.a = a;
     return r;
@@ -216,6 +217,61 @@ __device__ __forceinline__ void stage_records(const Geometry& g, const float* __
     }
 }
 
+// Record of the fast path: fractions, the coordinate slopes times the
+// attention weight, and the four corners' element offsets in value
+// (no_corner<T>() for a corner outside the level).
+struct BwdFastRecord {
+    float fx, fy;
+    float akx, aky;  // A * d(pixel)/d(location), 0 where border clamped
+    int4 o;          // corners (x0,y0), (x0+1,y0), (x0,y0+1), (x0+1,y0+1)
+};
+static_assert(sizeof(BwdFastRecord) == 2 * sizeof(float4), "records must tile two float4 slots");
+
+// Stage one fast-path record per (unit, sample) of the chunk [s0, s0 + sc),
+// and (with ws) the per-sample anchor and record of the grad_value pass.
+template <typename T>
+__device__ __forceinline__ void stage_fast_records(const Geometry& g, const float* __restrict__ loc,
+                                                   const float* __restrict__ attn, BwdFastRecord* s_rec, int row,
+                                                   int u0, int upb, int s0, int sc, AnchorWs ws)
+{
+    const int32_t nc = no_corner<T>();
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
+        const int gi = i / sc;
+        const int s = i - gi * sc;
+        const int uu = u0 + gi;
+        BwdFastRecord f = {0.f, 0.f, 0.f, 0.f, make_int4(nc, nc, nc, nc)};
+        if (uu < g.units) {
+            const UnitIdx ui = unit_index(g, uu);
+            const int si = s0 + s;
+            const int l = si / g.Np;
+            int H, W, start;
+            level_of(g.lv, l, H, W, start);
+            float ux, uy;
+            read_loc(g, loc, ui.b, ui.q, ui.h, si, ux, uy);
+            const float a = attn[((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si];
+            int x0, y0;
+            const BwdRecord r = make_record(g, ux, uy, a, H, W, start, x0, y0);
+            const int o00 = value_slab_offset(g, ui.b, ui.h) + r.off;
+            f.fx = r.fx;
+            f.fy = r.fy;
+            f.akx = a * r.kx;
+            f.aky = a * r.ky;
+            f.o.x = (r.mask & 1) ? o00 : nc;
+            f.o.y = (r.mask & 2) ? o00 + pstride : nc;
+            f.o.z = (r.mask & 4) ? o00 + r.rowp : nc;
+            f.o.w = (r.mask & 8) ? o00 + r.rowp + pstride : nc;
+            if (ws.anchor) {
+                const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
+                const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
+                ws.anchor[k] = an;
+                ws.rec[k] = make_float4(__uint_as_float(an), r.fx, r.fy, a);
+            }
+        }
+        s_rec[gi * row + s] = f;
+    }
+}
+
 // Write grad_A and grad_loc of the chunk from LDS with coalesced stores.
 __device__ __forceinline__ void store_results(const Geometry& g, const float4* s_res, int row, int u0, int upb,
                                               int s0, int sc, float* __restrict__ grad_loc,
@@ -250,8 +306,8 @@ __device__ __forceinline__ void store_results(const Geometry& g, const float4* s
 // ---------------------------------------------------------------------------
 // Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, channel rows
 // aligned to 4 elements. LPU lanes per unit, 4 channels per lane.
-template <typename T, int LPU>
-__global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max,
+template <typename T, int LPU, bool BUF>
+__global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max, int64_t value_bytes,
                                                                const T* __restrict__ grad_out,
                                                                const T* __restrict__ value,
                                                                const float* __restrict__ loc,
@@ -264,13 +320,15 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 
     extern __shared__ float4 smem[];
     const int row = sc_max + 1;
-    BwdRecord* s_rec = reinterpret_cast<BwdRecord*>(smem);
+    BwdFastRecord* s_rec = reinterpret_cast<BwdFastRecord*>(smem);
     float4* s_res = smem + 2 * upb * row;
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
     const bool want_dots = grad_loc != nullptr || grad_attn != nullptr;
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    const __amdgpu_buffer_rsrc_t vr = value_rsrc(value, BUF ? value_bytes : 0);
+    const int32_t nc = no_corner<T>();
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int u = u0 + grp;
@@ -278,7 +336,6 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
     const int c0 = lig * VEC;
     const bool lane_ok = unit_ok && c0 < g.Ch;
-    const T* vslab = value + value_slab_offset(g, ui.b, ui.h) + c0;
     float G[VEC] = {0.f, 0.f, 0.f, 0.f};
     if (lane_ok && want_dots)
         VecIO<T, VEC>::load(grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch + c0, G);
@@ -286,30 +343,40 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
-        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, ws);
+        stage_fast_records<T>(g, loc, attn, s_rec, row, u0, upb, s0, sc, ws);
         if (!want_dots) continue;
         __syncthreads();
         if (unit_ok) {
             for (int s = 0; s < sc; ++s) {
-                const BwdRecord r = s_rec[grp * row + s];
+                const BwdFastRecord r = s_rec[grp * row + s];
+                const int ok[4] = {r.o.x, r.o.y, r.o.z, r.o.w};
+                float v[4][VEC];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if constexpr (BUF) {
+                        BufIO<T, VEC>::load(vr, (uint32_t)(ok[k] + c0) * (uint32_t)sizeof(T), v[k]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) v[k][i] = 0.f;
+                        if (lane_ok && ok[k] != nc) VecIO<T, VEC>::load(value + ok[k] + c0, v[k]);
+                    }
+                }
+                if (BUF && !lane_ok) {
+                    // channels past C_h: read as zero (G is zero there too)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) v[k][i] = 0.f;
+                }
                 const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
                 const float w00 = gxw * gyw, w01 = r.fx * gyw, w10 = gxw * r.fy, w11 = r.fx * r.fy;
-                const int o00 = r.pix * pstride;
-                const int o10 = o00 + r.W * pstride;
-                float v00[VEC] = {0.f, 0.f, 0.f, 0.f}, v01[VEC] = {0.f, 0.f, 0.f, 0.f};
-                float v10[VEC] = {0.f, 0.f, 0.f, 0.f}, v11[VEC] = {0.f, 0.f, 0.f, 0.f};
-                if (lane_ok) {
-                    if (r.mask & 1) VecIO<T, VEC>::load(vslab + o00, v00);
-                    if (r.mask & 2) VecIO<T, VEC>::load(vslab + o00 + pstride, v01);
-                    if (r.mask & 4) VecIO<T, VEC>::load(vslab + o10, v10);
-                    if (r.mask & 8) VecIO<T, VEC>::load(vslab + o10 + pstride, v11);
-                }
                 float pa = 0.f, px = 0.f, py = 0.f;
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
-                    const float dx = gyw * (v01[i] - v00[i]) + r.fy * (v11[i] - v10[i]);
-                    const float dy = gxw * (v10[i] - v00[i]) + r.fx * (v11[i] - v01[i]);
+                    const float v00 = v[0][i], v01 = v[1][i], v10 = v[2][i], v11 = v[3][i];
+                    const float smp = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
+                    const float dx = gyw * (v01 - v00) + r.fy * (v11 - v10);
+                    const float dy = gxw * (v10 - v00) + r.fx * (v11 - v01);
                     pa = __builtin_fmaf(G[i], smp, pa);
                     px = __builtin_fmaf(G[i], dx, px);
                     py = __builtin_fmaf(G[i], dy, py);
@@ -317,7 +384,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
                 pa = group_sum<LPU>(pa);
                 px = group_sum<LPU>(px);
                 py = group_sum<LPU>(py);
-                if (lig == 0) s_res[grp * row + s] = make_float4(pa, r.a * px * r.kx, r.a * py * r.ky, 0.f);
+                if (lig == 0) s_res[grp * row + s] = make_float4(pa, r.akx * px, r.aky * py, 0.f);
             }
         }
         __syncthreads();
@@ -918,9 +985,9 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
                 const BwdRecord r = s_rec[grp * row + s];
                 const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
                 const float w00 = gxw * gyw, w01 = r.fx * gyw, w10 = gxw * r.fy, w11 = r.fx * r.fy;
-                const int o00 = r.pix * pstride;
+                const int o00 = r.off;
                 const int o01 = o00 + pstride;
-                const int o10 = o00 + r.W * pstride;
+                const int o10 = o00 + r.rowp;
                 const int o11 = o10 + pstride;
                 float pa = 0.f, px = 0.f, py = 0.f;
                 for (int c = lig; c < g.Ch; c += LPU) {
@@ -1002,10 +1069,16 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
 {
     constexpr int upb = kBlock / LPU;
     const int sc = samples_per_chunk(g.S, upb);
-    const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
-    hipLaunchKernelGGL((backward_fast_kernel<T, LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                       static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn, grad_loc,
-                       grad_attn, ws);
+    const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdFastRecord) + sizeof(float4));
+    const int64_t value_bytes = (int64_t)g.B * g.L * g.Nh * g.Ch * (int64_t)sizeof(T);
+    if (buffer_loads_ok(value_bytes))
+        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                           value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn,
+                           grad_loc, grad_attn, ws);
+    else
+        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                           value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn,
+                           grad_loc, grad_attn, ws);
     return hipGetLastError();
 }
 

@@ -201,22 +201,95 @@ template <int VEC> struct VecIO<uint16_t, VEC> {
 };
 
 // ---------------------------------------------------------------------------
+// Buffer loads. A raw buffer resource over `value` (base, byte size) makes the
+// hardware range-check every load: an offset at or past the size returns
+// zeros without touching memory. The gathers use it for corners that must
+// read nothing (outside the level, or zero weight), with no branch and no
+// zero fill. Used when value is smaller than 2^31 - 2^20 bytes (offsets are
+// 32-bit byte offsets); larger tensors take the pointer path.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t value_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// Element offset that marks "no corner": times the element size it is 2^31,
+// past every byte offset a buffer load may legitimately use.
+template <typename T>
+__host__ __device__ constexpr int32_t no_corner()
+{
+    return (int32_t)((1u << 31) / sizeof(T));
+}
+
+// Whether a value tensor of `bytes` bytes takes the buffer-load path.
+__host__ __device__ inline bool buffer_loads_ok(int64_t bytes) { return bytes <= ((int64_t)1 << 31) - ((int64_t)1 << 20); }
+
+// Load VEC elements of T at byte offset `off` of the buffer as float32.
+template <typename T, int VEC> struct BufIO;
+
+template <int VEC> struct BufIO<float, VEC> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[VEC])
+    {
+        if constexpr (VEC == 4) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+            v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+            v[2] = __uint_as_float(t[2]); v[3] = __uint_as_float(t[3]);
+        } else if constexpr (VEC == 2) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0));
+        }
+    }
+};
+
+template <int VEC> struct BufIO<uint16_t, VEC> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[VEC])
+    {
+        if constexpr (VEC == 8) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(t[i] << 16);
+                v[2 * i + 1] = __uint_as_float(t[i] & 0xffff0000u);
+            }
+        } else if constexpr (VEC == 4) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            v[0] = __uint_as_float(t[0] << 16); v[1] = __uint_as_float(t[0] & 0xffff0000u);
+            v[2] = __uint_as_float(t[1] << 16); v[3] = __uint_as_float(t[1] & 0xffff0000u);
+        } else if constexpr (VEC == 2) {
+            const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+            v[0] = __uint_as_float(t << 16); v[1] = __uint_as_float(t & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                v[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, 0) << 16);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // Forward sampling of one unit, shared by the sampler and the fused
 // producer + sampler kernels.
 
-// Gather record of one sample: the anchor corner's pixel and its level's row
-// length (the four bilinear weights travel beside it as a float4).
-struct FwdRecordPix {
-    int32_t pix;   // flat pixel index (along L) of corner (x0, y0)
-    int32_t W;     // row length of the sample's level, in pixels
+// Gather record of one sample: the four corner weights (x0,y0), (x0+1,y0),
+// (x0,y0+1), (x0+1,y0+1) premultiplied by the attention weight (0 for a
+// corner outside the level), and the element offsets in value of those
+// corners' first channel of the sample's (b, h); no_corner<T>() where the
+// weight is 0.
+struct FwdRecord {
+    float4 w;
+    int4 o;
 };
 
 // Coordinate map, padding and bilinear corners of one sample at normalised
-// (ux, uy) of level (H, W, start) with attention weight a: w holds the four
-// corner weights (x0,y0), (x0+1,y0), (x0,y0+1), (x0+1,y0+1) premultiplied by
-// a, 0 for a corner outside the level.
+// (ux, uy) of level (H, W, start) with attention weight a, for the (b, h)
+// slab starting at element slab_off of value.
+template <typename T>
 __device__ __forceinline__ void sampler_record(const Geometry& g, float ux, float uy, float a, int H, int W,
-                                               int start, float4& w, FwdRecordPix& rp)
+                                               int start, int slab_off, FwdRecord& rec)
 {
     float x = pixel_coord(ux, W, g.align_corners);
     float y = pixel_coord(uy, H, g.align_corners);
@@ -236,47 +309,48 @@ __device__ __forceinline__ void sampler_record(const Geometry& g, float ux, floa
     const bool ix0 = x0 >= 0 && x0 < W, ix1 = x0 >= -1 && x0 + 1 < W;
     const bool iy0 = y0 >= 0 && y0 < H, iy1 = y0 >= -1 && y0 + 1 < H;
     const float gx = 1.f - fx, gy = 1.f - fy;
+    float4 w;
     w.x = (ix0 && iy0) ? a * (gx * gy) : 0.f;
     w.y = (ix1 && iy0) ? a * (fx * gy) : 0.f;
     w.z = (ix0 && iy1) ? a * (gx * fy) : 0.f;
     w.w = (ix1 && iy1) ? a * (fx * fy) : 0.f;
-    rp.pix = start + y0 * W + x0;
-    rp.W = W;
+    // unsigned arithmetic: offsets of corners outside the level may wrap; they are replaced below
+    const uint32_t pstride = (uint32_t)(g.bnlc ? g.Ch : g.Nh * g.Ch);
+    const uint32_t o00 = (uint32_t)slab_off + (uint32_t)(start + y0 * W + x0) * pstride;
+    const uint32_t orow = (uint32_t)W * pstride;
+    const int32_t nc = no_corner<T>();
+    rec.w = w;
+    rec.o.x = w.x != 0.f ? (int32_t)o00 : nc;
+    rec.o.y = w.y != 0.f ? (int32_t)(o00 + pstride) : nc;
+    rec.o.z = w.z != 0.f ? (int32_t)(o00 + orow) : nc;
+    rec.o.w = w.w != 0.f ? (int32_t)(o00 + orow + pstride) : nc;
 }
 
-// Accumulate sc staged samples of one unit into acc: VEC channels per lane,
-// loading only the corners whose weight is nonzero. `slab` points at the
-// lane's first channel of the unit's (b, h) slab; pstride is the element
-// distance between neighbouring pixels.
-template <typename T, int VEC>
-__device__ __forceinline__ void gather_samples(const T* slab, int pstride, const float4* rw,
-                                               const FwdRecordPix* rpix, int sc, float (&acc)[VEC])
+// Accumulate sc staged samples of one unit into acc: VEC channels per lane
+// starting at channel c0. BUF: every corner is a buffer load (a no-corner
+// offset returns zeros, so the multiply-add is a no-op); otherwise only the
+// corners with nonzero weight are loaded through `value`.
+template <typename T, int VEC, bool BUF>
+__device__ __forceinline__ void gather_samples(const T* value, __amdgpu_buffer_rsrc_t vr, int c0, const FwdRecord* rec,
+                                               int sc, float (&acc)[VEC])
 {
 #pragma unroll 4
     for (int s = 0; s < sc; ++s) {
-        const float4 w = rw[s];
-        const FwdRecordPix rp = rpix[s];
-        const T* p00 = slab + rp.pix * pstride;
-        float v[VEC];
-        if (w.x != 0.f) {
-            VecIO<T, VEC>::load(p00, v);
+        const FwdRecord r = rec[s];
+        const float wk[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+        const int ok[4] = {r.o.x, r.o.y, r.o.z, r.o.w};
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.x, v[i], acc[i]);
-        }
-        if (w.y != 0.f) {
-            VecIO<T, VEC>::load(p00 + pstride, v);
+        for (int k = 0; k < 4; ++k) {
+            float v[VEC];
+            if constexpr (BUF) {
+                BufIO<T, VEC>::load(vr, (uint32_t)(ok[k] + c0) * (uint32_t)sizeof(T), v);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.y, v[i], acc[i]);
-        }
-        if (w.z != 0.f) {
-            VecIO<T, VEC>::load(p00 + rp.W * pstride, v);
+                for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(wk[k], v[i], acc[i]);
+            } else if (wk[k] != 0.f) {
+                VecIO<T, VEC>::load(value + ok[k] + c0, v);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.z, v[i], acc[i]);
-        }
-        if (w.w != 0.f) {
-            VecIO<T, VEC>::load(p00 + (rp.W + 1) * pstride, v);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(w.w, v[i], acc[i]);
+                for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(wk[k], v[i], acc[i]);
+            }
         }
     }
 }

@@ -16,15 +16,19 @@
 //  - per chunk of up to SC samples, the workgroup first stages every sample
 //    of its units in LDS, one thread per (unit, sample): the coordinate map,
 //    padding, floor, the four bilinear weights premultiplied by the attention
-//    weight (0 for a corner outside the level) and the corner's pixel index;
-//  - then each lane walks the staged samples and issues only the corner
-//    loads whose weight is nonzero, accumulating in float32 registers.
+//    weight (0 for a corner outside the level) and the four corners' element
+//    offsets in value (a "no corner" mark where the weight is 0);
+//  - then each lane walks the staged samples and loads the corners, as
+//    range-checked buffer loads (a no-corner offset lies past the end of the
+//    buffer and returns zeros without a memory access, so there is no branch)
+//    or, for value tensors of 2^31 bytes and more, as plain loads of the
+//    nonzero-weight corners only; accumulation is float32 in registers.
 #include "msda_device.h"
 
 namespace msda {
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
+template <typename T, int VEC, bool BUF>
+__global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max, int64_t value_bytes,
                                                          const T* __restrict__ value,
                                                          const float* __restrict__ loc,
                                                          const float* __restrict__ attn,
@@ -34,13 +38,13 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
     const int lpu_log2 = g.lpu_log2;
     const int upb = kBlock >> lpu_log2;
     const int row = sc_max + 1;  // padded LDS row (one row per unit) against bank conflicts
-    float4* s_w = smem;
-    FwdRecordPix* s_pix = reinterpret_cast<FwdRecordPix*>(smem + upb * row);
+    FwdRecord* s_rec = reinterpret_cast<FwdRecord*>(smem);
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
     const int S = g.S;
     const int plane = g.Nq * g.Nh * S;  // distance between the x and y planes (B2QHLP)
+    const __amdgpu_buffer_rsrc_t vr = value_rsrc(value, BUF ? value_bytes : 0);
 
     // The unit this lane works on.
     const int grp = tid >> lpu_log2;
@@ -56,8 +60,6 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
     const int c0 = ((chunk << lpu_log2) + lig) * VEC;
     const bool active = (u < g.units) && (c0 < g.Ch);
     if (u >= g.units) { b = 0; h = 0; q = 0; }  // tail lanes: keep every address in range
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    const T* slab = value + (g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch) + c0;
 
     float acc[VEC];
 #pragma unroll
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
             const int gi = i / sc;
             const int s = i - gi * sc;
             const int uu = u0 + gi;
-            float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-            FwdRecordPix rp = {0, 1};
+            FwdRecord rec = {make_float4(0.f, 0.f, 0.f, 0.f),
+                             make_int4(no_corner<T>(), no_corner<T>(), no_corner<T>(), no_corner<T>())};
             if (uu < g.units) {
                 int t = uu / g.chunks;
                 const int qq = t % g.Nq; t /= g.Nq;
@@ -94,48 +96,52 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
                     ux = loc[2 * idx];
                     uy = loc[2 * idx + 1];
                 }
-                sampler_record(g, ux, uy, attn[idx], H, W, start, w, rp);
+                const int slab_off = g.bnlc ? (bb * g.Nh + hh) * g.L * g.Ch : bb * g.L * g.Nh * g.Ch + hh * g.Ch;
+                sampler_record<T>(g, ux, uy, attn[idx], H, W, start, slab_off, rec);
             }
-            s_w[gi * row + s] = w;
-            s_pix[gi * row + s] = rp;
+            s_rec[gi * row + s] = rec;
         }
         __syncthreads();
-        // ---- gather: VEC channels per lane, only corners with nonzero weight ----
-        if (active) gather_samples<T, VEC>(slab, pstride, s_w + grp * row, s_pix + grp * row, sc, acc);
+        // ---- gather: VEC channels per lane ----
+        if (active) gather_samples<T, VEC, BUF>(value, vr, c0, s_rec + grp * row, sc, acc);
     }
     if (active) VecIO<T, VEC>::store(out + ((b * g.Nq + q) * g.Nh + h) * g.Ch + c0, acc);
 }
 
 // Host launcher: grid/LDS sizing for one instantiation.
 template <typename T, int VEC>
-static hipError_t launch_forward_t(const Geometry& g, const void* value, const float* loc,
+static hipError_t launch_forward_t(const Geometry& g, int64_t value_bytes, const void* value, const float* loc,
                                    const float* attn, void* out, hipStream_t stream)
 {
     const int upb = kBlock >> g.lpu_log2;
-    const size_t rec = sizeof(float4) + sizeof(FwdRecordPix);
+    const size_t rec = sizeof(FwdRecord);
     int sc = g.S < 16 ? g.S : 16;
     while (sc > 1 && (size_t)upb * (sc + 1) * rec > kLdsBudget) --sc;
     const size_t lds = (size_t)upb * (sc + 1) * rec;
-    hipLaunchKernelGGL((forward_kernel<T, VEC>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                       static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
+    if (buffer_loads_ok(value_bytes))
+        hipLaunchKernelGGL((forward_kernel<T, VEC, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                           value_bytes, static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
+    else
+        hipLaunchKernelGGL((forward_kernel<T, VEC, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                           value_bytes, static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const Geometry& g, int bf16, int vec, const void* value, const float* loc,
-                          const float* attn, void* out, hipStream_t stream)
+hipError_t launch_forward(const Geometry& g, int bf16, int vec, int64_t value_bytes, const void* value,
+                          const float* loc, const float* attn, void* out, hipStream_t stream)
 {
     if (bf16) {
         switch (vec) {
-        case 8: return launch_forward_t<uint16_t, 8>(g, value, loc, attn, out, stream);
-        case 4: return launch_forward_t<uint16_t, 4>(g, value, loc, attn, out, stream);
-        case 2: return launch_forward_t<uint16_t, 2>(g, value, loc, attn, out, stream);
-        default: return launch_forward_t<uint16_t, 1>(g, value, loc, attn, out, stream);
+        case 8: return launch_forward_t<uint16_t, 8>(g, value_bytes, value, loc, attn, out, stream);
+        case 4: return launch_forward_t<uint16_t, 4>(g, value_bytes, value, loc, attn, out, stream);
+        case 2: return launch_forward_t<uint16_t, 2>(g, value_bytes, value, loc, attn, out, stream);
+        default: return launch_forward_t<uint16_t, 1>(g, value_bytes, value, loc, attn, out, stream);
         }
     }
     switch (vec) {
-    case 4: return launch_forward_t<float, 4>(g, value, loc, attn, out, stream);
-    case 2: return launch_forward_t<float, 2>(g, value, loc, attn, out, stream);
-    default: return launch_forward_t<float, 1>(g, value, loc, attn, out, stream);
+    case 4: return launch_forward_t<float, 4>(g, value_bytes, value, loc, attn, out, stream);
+    case 2: return launch_forward_t<float, 2>(g, value_bytes, value, loc, attn, out, stream);
+    default: return launch_forward_t<float, 1>(g, value_bytes, value, loc, attn, out, stream);
     }
 }
 

@@ -75,7 +75,8 @@ int producer_weight_col_blocks(int D);
 hipError_t launch_producer_forward(const Geometry& g, const ProducerGeom& pg, int bf16, const ProducerArgsRaw& a,
                                    float* loc, float* attn, hipStream_t stream);
 hipError_t launch_fused_forward(const Geometry& g, const ProducerGeom& pg, int bf16, int vec, const ProducerArgsRaw& a,
-                                const void* value, void* out, float* loc, float* attn, hipStream_t stream);
+                                int64_t value_bytes, const void* value, void* out, float* loc, float* attn,
+                                hipStream_t stream);
 hipError_t launch_producer_backward(const Geometry& g, const ProducerGeom& pg, int bf16, const ProducerArgsRaw& a,
                                     const ProducerGradIn& in, const ProducerGradOut& o, void* workspace,
                                     hipStream_t stream);

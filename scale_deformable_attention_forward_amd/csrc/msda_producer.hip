@@ -338,16 +338,16 @@ __global__ __launch_bounds__(kBlock) void producer_forward_kernel(Geometry g, Pr
 // each XCD sweeps a contiguous range of them (as in the sampler). Dynamic
 // LDS: the projection phase, then (over the same bytes, once the epilogue
 // holds its inputs in registers) the gather records of the 64 queries
-// (float4 weights and FwdRecordPix, rows of S + 1 against bank conflicts).
-template <typename T, int VEC, int CTM>
+// (FwdRecord, rows of S + 1 against bank conflicts).
+template <typename T, int VEC, int CTM, bool BUF>
 __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, ProducerGeom pg, ProducerArgs<T> a,
-                                                               const T* __restrict__ value, T* __restrict__ out,
-                                                               float* __restrict__ loc, float* __restrict__ attn)
+                                                               int64_t value_bytes, const T* __restrict__ value,
+                                                               T* __restrict__ out, float* __restrict__ loc,
+                                                               float* __restrict__ attn)
 {
     extern __shared__ float4 smem4[];
     const int row = pg.S + 1;
-    float4* s_rw = smem4;
-    FwdRecordPix* s_rp = reinterpret_cast<FwdRecordPix*>(s_rw + kPRows * row);
+    FwdRecord* s_rec = reinterpret_cast<FwdRecord*>(smem4);
     float* s_x = reinterpret_cast<float*>(smem4);
     float* s_w = s_x + kPRows * kPStride;
     float* s_o = s_x;
@@ -369,15 +369,12 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
     HeadOut<CTM> ho;
     ho.load(g, pg, s_o, ost, a.b_off, a.b_att, a.ref + (size_t)m0 * pg.Nl * 2, rows_valid, h);
     __syncthreads();  // s_o is in registers: the records take its place
+    const int slab_off = g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch;
     ho.finish(pg, rows_valid, [&](int r, int j, int l, float ux, float uy, float A) {
         if (loc || attn) store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
         int H, W, start;
         level_of(g.lv, l, H, W, start);
-        float4 w;
-        FwdRecordPix rp;
-        sampler_record(g, ux, uy, A, H, W, start, w, rp);
-        s_rw[r * row + j] = w;
-        s_rp[r * row + j] = rp;
+        sampler_record<T>(g, ux, uy, A, H, W, start, slab_off, s_rec[r * row + j]);
     });
     __syncthreads();
 
@@ -385,8 +382,7 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
     const int lpu_log2 = g.lpu_log2;
     const int upb = kBlock >> lpu_log2;
     const int grp = threadIdx.x >> lpu_log2, lig = threadIdx.x & ((1 << lpu_log2) - 1);
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    const T* slab_v = value + (g.bnlc ? (b * g.Nh + h) * g.L * g.Ch : b * g.L * g.Nh * g.Ch + h * g.Ch);
+    const __amdgpu_buffer_rsrc_t vr = value_rsrc(value, BUF ? value_bytes : 0);
     for (int u = grp; u < rows_valid * g.chunks; u += upb) {
         const int r = u / g.chunks, chunk = u - r * g.chunks;
         const int c0 = ((chunk << lpu_log2) + lig) * VEC;
@@ -394,7 +390,7 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
         float o[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = 0.f;
-        gather_samples<T, VEC>(slab_v + c0, pstride, s_rw + r * row, s_rp + r * row, pg.S, o);
+        gather_samples<T, VEC, BUF>(value, vr, c0, s_rec + r * row, pg.S, o);
         VecIO<T, VEC>::store(out + ((size_t)(m0 + r) * g.Nh + h) * g.Ch + c0, o);
     }
 }
@@ -698,7 +694,7 @@ size_t producer_forward_lds(const ProducerGeom& pg) { return (size_t)projection_
 
 size_t fused_forward_lds(const ProducerGeom& pg)
 {
-    const size_t records = (size_t)kPRows * (pg.S + 1) * (sizeof(float4) + sizeof(FwdRecordPix));
+    const size_t records = (size_t)kPRows * (pg.S + 1) * sizeof(FwdRecord);
     return records > producer_forward_lds(pg) ? records : producer_forward_lds(pg);
 }
 
@@ -755,36 +751,45 @@ hipError_t launch_producer_forward(const Geometry& g, const ProducerGeom& pg, in
     return hipGetLastError();
 }
 
-template <typename T, int VEC>
-static void launch_fused_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, const void* value,
-                           void* out, float* loc, float* attn, hipStream_t stream)
+template <typename T, int VEC, int CTM>
+static void launch_fused_c(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, int64_t value_bytes,
+                           const void* value, void* out, float* loc, float* attn, hipStream_t stream)
 {
     const int qtiles = (g.Nq + kPRows - 1) / kPRows;
     const dim3 grid(g.B * g.Nh * qtiles);
     const size_t lds = fused_forward_lds(pg);
-    if (pg.ct == 3)
-        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, 3>), grid, dim3(kBlock), lds, stream, g, pg, typed<T>(a),
-                           static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
+    if (buffer_loads_ok(value_bytes))
+        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, CTM, true>), grid, dim3(kBlock), lds, stream, g, pg,
+                           typed<T>(a), value_bytes, static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
     else
-        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, 6>), grid, dim3(kBlock), lds, stream, g, pg, typed<T>(a),
-                           static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
+        hipLaunchKernelGGL((fused_forward_kernel<T, VEC, CTM, false>), grid, dim3(kBlock), lds, stream, g, pg,
+                           typed<T>(a), value_bytes, static_cast<const T*>(value), static_cast<T*>(out), loc, attn);
+}
+
+template <typename T, int VEC>
+static void launch_fused_t(const Geometry& g, const ProducerGeom& pg, const ProducerArgsRaw& a, int64_t value_bytes,
+                           const void* value, void* out, float* loc, float* attn, hipStream_t stream)
+{
+    if (pg.ct == 3) launch_fused_c<T, VEC, 3>(g, pg, a, value_bytes, value, out, loc, attn, stream);
+    else launch_fused_c<T, VEC, 6>(g, pg, a, value_bytes, value, out, loc, attn, stream);
 }
 
 hipError_t launch_fused_forward(const Geometry& g, const ProducerGeom& pg, int bf16, int vec, const ProducerArgsRaw& a,
-                                const void* value, void* out, float* loc, float* attn, hipStream_t stream)
+                                int64_t value_bytes, const void* value, void* out, float* loc, float* attn,
+                                hipStream_t stream)
 {
     if (bf16) {
         switch (vec) {
-        case 8: launch_fused_t<uint16_t, 8>(g, pg, a, value, out, loc, attn, stream); break;
-        case 4: launch_fused_t<uint16_t, 4>(g, pg, a, value, out, loc, attn, stream); break;
-        case 2: launch_fused_t<uint16_t, 2>(g, pg, a, value, out, loc, attn, stream); break;
-        default: launch_fused_t<uint16_t, 1>(g, pg, a, value, out, loc, attn, stream); break;
+        case 8: launch_fused_t<uint16_t, 8>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
+        case 4: launch_fused_t<uint16_t, 4>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
+        case 2: launch_fused_t<uint16_t, 2>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
+        default: launch_fused_t<uint16_t, 1>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
         }
     } else {
         switch (vec) {
-        case 4: launch_fused_t<float, 4>(g, pg, a, value, out, loc, attn, stream); break;
-        case 2: launch_fused_t<float, 2>(g, pg, a, value, out, loc, attn, stream); break;
-        default: launch_fused_t<float, 1>(g, pg, a, value, out, loc, attn, stream); break;
+        case 4: launch_fused_t<float, 4>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
+        case 2: launch_fused_t<float, 2>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
+        default: launch_fused_t<float, 1>(g, pg, a, value_bytes, value, out, loc, attn, stream); break;
         }
     }
     return hipGetLastError();
