@@ -116,6 +116,10 @@ msda_status check_problem(const msda_problem* p, Geometry* g, Sizes* z)
         g->lv.W[l] = in ? (int32_t)p->spatial_shapes[2 * l + 1] : 1;
         g->lv.start[l] = in ? (int32_t)p->level_start_index[l] : 0;
     }
+    g->nq_div = msda::make_fastdiv((uint32_t)g->Nq);
+    g->nh_div = msda::make_fastdiv((uint32_t)g->Nh);
+    g->np_div = msda::make_fastdiv((uint32_t)g->Np);
+    g->ch_div = msda::make_fastdiv(1);
     return MSDA_OK;
 }
 
@@ -362,6 +366,7 @@ msda_status msda_forward(const msda_problem* problem, const void* value, const f
     g.lpu_log2 = ilog2(lanes);
     const int64_t per_chunk = ((int64_t)1 << g.lpu_log2) * vec;
     g.chunks = (int32_t)((problem->C_h + per_chunk - 1) / per_chunk);
+    g.ch_div = msda::make_fastdiv((uint32_t)g.chunks);
     const int64_t units = (int64_t)g.B * g.Nh * g.Nq * g.chunks;
     const int64_t upb = msda::kBlock >> g.lpu_log2;
     if (units >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
@@ -535,6 +540,7 @@ msda_status msda_fused_forward(const msda_problem* problem, int64_t D, const voi
     g.lpu_log2 = ilog2(lanes);
     const int64_t per_chunk = ((int64_t)1 << g.lpu_log2) * vec;
     g.chunks = (int32_t)((problem->C_h + per_chunk - 1) / per_chunk);
+    g.ch_div = msda::make_fastdiv((uint32_t)g.chunks);
     g.units = 0;
     g.blocks = 0;
     pg.vec = producer_vec(D, z.elem, {query, offset_weight, attention_weight});

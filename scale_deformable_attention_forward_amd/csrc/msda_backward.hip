@@ -104,10 +104,10 @@ struct UnitIdx {
 __device__ __forceinline__ UnitIdx unit_index(const Geometry& g, int u)
 {
     UnitIdx r;
-    r.q = u % g.Nq;
-    const int t = u / g.Nq;
-    r.h = t % g.Nh;
-    r.b = t / g.Nh;
+    const int t = fdiv(u, g.nq_div);
+    r.q = u - t * g.Nq;
+    r.b = fdiv(t, g.nh_div);
+    r.h = t - r.b * g.Nh;
     return r;
 }
 
@@ -188,19 +188,20 @@ struct AnchorWs {
 // Stage one record per (unit, sample) of the chunk [s0, s0 + sc).
 __device__ __forceinline__ void stage_records(const Geometry& g, const float* __restrict__ loc,
                                               const float* __restrict__ attn, BwdRecord* s_rec, int row,
-                                              int u0, int upb, int s0, int sc, AnchorWs ws)
+                                              int u0, int upb, int s0, int sc, const FastDiv& scd,
+                                              const int4* s_lv, AnchorWs ws)
 {
     for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
-        const int gi = i / sc;
+        const int gi = fdiv(i, scd);
         const int s = i - gi * sc;
         const int uu = u0 + gi;
         BwdRecord r = {0.f, 0.f, 0.f, 0.f, 0, 1, 0, 0.f};
         if (uu < g.units) {
             const UnitIdx ui = unit_index(g, uu);
             const int si = s0 + s;
-            const int l = si / g.Np;
-            int H, W, start;
-            level_of(g.lv, l, H, W, start);
+            const int l = fdiv(si, g.np_div);
+            const int4 lvl = s_lv[l];
+            const int H = lvl.x, W = lvl.y, start = lvl.z;
             float ux, uy;
             read_loc(g, loc, ui.b, ui.q, ui.h, si, ux, uy);
             const float a = attn[((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si];
@@ -232,21 +233,22 @@ static_assert(sizeof(BwdFastRecord) == 2 * sizeof(float4), "records must tile tw
 template <typename T>
 __device__ __forceinline__ void stage_fast_records(const Geometry& g, const float* __restrict__ loc,
                                                    const float* __restrict__ attn, BwdFastRecord* s_rec, int row,
-                                                   int u0, int upb, int s0, int sc, AnchorWs ws)
+                                                   int u0, int upb, int s0, int sc, const FastDiv& scd,
+                                                   const int4* s_lv, AnchorWs ws)
 {
     const int32_t nc = no_corner<T>();
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
-        const int gi = i / sc;
+        const int gi = fdiv(i, scd);
         const int s = i - gi * sc;
         const int uu = u0 + gi;
         BwdFastRecord f = {0.f, 0.f, 0.f, 0.f, make_int4(nc, nc, nc, nc)};
         if (uu < g.units) {
             const UnitIdx ui = unit_index(g, uu);
             const int si = s0 + s;
-            const int l = si / g.Np;
-            int H, W, start;
-            level_of(g.lv, l, H, W, start);
+            const int l = fdiv(si, g.np_div);
+            const int4 lvl = s_lv[l];
+            const int H = lvl.x, W = lvl.y, start = lvl.z;
             float ux, uy;
             read_loc(g, loc, ui.b, ui.q, ui.h, si, ux, uy);
             const float a = attn[((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si];
@@ -274,11 +276,11 @@ __device__ __forceinline__ void stage_fast_records(const Geometry& g, const floa
 
 // Write grad_A and grad_loc of the chunk from LDS with coalesced stores.
 __device__ __forceinline__ void store_results(const Geometry& g, const float4* s_res, int row, int u0, int upb,
-                                              int s0, int sc, float* __restrict__ grad_loc,
+                                              int s0, int sc, const FastDiv& scd, float* __restrict__ grad_loc,
                                               float* __restrict__ grad_attn)
 {
     for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
-        const int gi = i / sc;
+        const int gi = fdiv(i, scd);
         const int s = i - gi * sc;
         const int uu = u0 + gi;
         if (uu >= g.units) continue;
@@ -307,7 +309,8 @@ __device__ __forceinline__ void store_results(const Geometry& g, const float4* s
 // Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, channel rows
 // aligned to 4 elements. LPU lanes per unit, 4 channels per lane.
 template <typename T, int LPU, bool BUF>
-__global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max, int64_t value_bytes,
+__global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max, ChunkDiv cdiv,
+                                                               int64_t value_bytes,
                                                                const T* __restrict__ grad_out,
                                                                const T* __restrict__ value,
                                                                const float* __restrict__ loc,
@@ -322,6 +325,8 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const int row = sc_max + 1;
     BwdFastRecord* s_rec = reinterpret_cast<BwdFastRecord*>(smem);
     float4* s_res = smem + 2 * upb * row;
+    __shared__ int4 s_lv[kMaxLevels];
+    fill_level_table(g.lv, s_lv);
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
@@ -343,7 +348,8 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
-        stage_fast_records<T>(g, loc, attn, s_rec, row, u0, upb, s0, sc, ws);
+        const FastDiv& scd = cdiv.of(sc, sc_max);
+        stage_fast_records<T>(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv, ws);
         if (!want_dots) continue;
         __syncthreads();
         if (unit_ok) {
@@ -368,19 +374,19 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) v[k][i] = 0.f;
                 }
-                const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
-                const float w00 = gxw * gyw, w01 = r.fx * gyw, w10 = gxw * r.fy, w11 = r.fx * r.fy;
-                float pa = 0.f, px = 0.f, py = 0.f;
+                // the three dot products are linear in the four corner rows: form this
+                // lane's <G, v_k> for each corner k, then combine them
+                float d[4];
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    const float v00 = v[0][i], v01 = v[1][i], v10 = v[2][i], v11 = v[3][i];
-                    const float smp = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
-                    const float dx = gyw * (v01 - v00) + r.fy * (v11 - v10);
-                    const float dy = gxw * (v10 - v00) + r.fx * (v11 - v01);
-                    pa = __builtin_fmaf(G[i], smp, pa);
-                    px = __builtin_fmaf(G[i], dx, px);
-                    py = __builtin_fmaf(G[i], dy, py);
+                for (int k = 0; k < 4; ++k) {
+                    d[k] = G[0] * v[k][0];
+#pragma unroll
+                    for (int i = 1; i < VEC; ++i) d[k] = __builtin_fmaf(G[i], v[k][i], d[k]);
                 }
+                const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
+                float pa = gxw * gyw * d[0] + r.fx * gyw * d[1] + gxw * r.fy * d[2] + r.fx * r.fy * d[3];
+                float px = gyw * (d[1] - d[0]) + r.fy * (d[3] - d[2]);
+                float py = gxw * (d[2] - d[0]) + r.fx * (d[3] - d[1]);
                 pa = group_sum<LPU>(pa);
                 px = group_sum<LPU>(px);
                 py = group_sum<LPU>(py);
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
             }
         }
         __syncthreads();
-        store_results(g, s_res, row, u0, upb, s0, sc, grad_loc, grad_attn);
+        store_results(g, s_res, row, u0, upb, s0, sc, scd, grad_loc, grad_attn);
     }
 }
 
@@ -945,7 +951,7 @@ __global__ __launch_bounds__(kBlock) void band_reduce_kernel(Geometry g, TilePla
 // unit, channels beyond LPU in a loop); grad_value via float atomics into
 // `gacc` (grad_value itself for float32, a float32 workspace for bfloat16).
 template <typename T, int LPU>
-__global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, int sc_max,
+__global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, int sc_max, ChunkDiv cdiv,
                                                                   const T* __restrict__ grad_out,
                                                                   const T* __restrict__ value,
                                                                   const float* __restrict__ loc,
@@ -959,6 +965,8 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const int row = sc_max + 1;
     BwdRecord* s_rec = reinterpret_cast<BwdRecord*>(smem);
     float4* s_res = smem + 2 * upb * row;
+    __shared__ int4 s_lv[kMaxLevels];
+    fill_level_table(g.lv, s_lv);
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
@@ -978,7 +986,8 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
-        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, no_ws);
+        const FastDiv& scd = cdiv.of(sc, sc_max);
+        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv, no_ws);
         __syncthreads();
         if (unit_ok) {
             for (int s = 0; s < sc; ++s) {
@@ -1022,7 +1031,7 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
         }
         if (!want_dots) continue;
         __syncthreads();
-        store_results(g, s_res, row, u0, upb, s0, sc, grad_loc, grad_attn);
+        store_results(g, s_res, row, u0, upb, s0, sc, scd, grad_loc, grad_attn);
     }
 }
 
@@ -1071,14 +1080,15 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
     const int sc = samples_per_chunk(g.S, upb);
     const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdFastRecord) + sizeof(float4));
     const int64_t value_bytes = (int64_t)g.B * g.L * g.Nh * g.Ch * (int64_t)sizeof(T);
+    const ChunkDiv cdiv = make_chunkdiv(g.S, sc);
     if (buffer_loads_ok(value_bytes))
         hipLaunchKernelGGL((backward_fast_kernel<T, LPU, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                           value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn,
-                           grad_loc, grad_attn, ws);
+                           cdiv, value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc,
+                           attn, grad_loc, grad_attn, ws);
     else
         hipLaunchKernelGGL((backward_fast_kernel<T, LPU, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
-                           value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn,
-                           grad_loc, grad_attn, ws);
+                           cdiv, value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc,
+                           attn, grad_loc, grad_attn, ws);
     return hipGetLastError();
 }
 
@@ -1104,6 +1114,7 @@ static hipError_t launch_generic_t(const Geometry& g, const void* grad_out, cons
     const int sc = samples_per_chunk(g.S, upb);
     const size_t lds = (size_t)upb * (sc + 1) * (sizeof(BwdRecord) + sizeof(float4));
     hipLaunchKernelGGL((backward_generic_kernel<T, LPU>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+                       make_chunkdiv(g.S, sc),
                        static_cast<const T*>(grad_out), static_cast<const T*>(value), loc, attn, gacc, grad_loc,
                        grad_attn);
     return hipGetLastError();

@@ -21,6 +21,42 @@ struct Levels {
     int32_t start[kMaxLevels];
 };
 
+// Division by a divisor fixed for a launch, as a multiply-high, an add and a
+// shift (the round-up method of division by invariant integers: with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, every n < 2^31
+// has n / d = (mulhi(n, m) + n) >> l). Built on the host, used by kernels in
+// place of a runtime integer division.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d)
+{
+    if (d < 1) d = 1;
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    const uint64_t m = ((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d) + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f)
+{
+    return (int)((__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.l);
+}
+
+// Divisions by the samples per staged chunk: a launch stages chunks of
+// sc_max samples and at most one shorter last chunk.
+struct ChunkDiv {
+    FastDiv full, tail;
+    __device__ __forceinline__ const FastDiv& of(int sc, int sc_max) const { return sc == sc_max ? full : tail; }
+};
+
+__host__ inline ChunkDiv make_chunkdiv(int S, int sc_max)
+{
+    const int rest = S % sc_max;
+    return ChunkDiv{make_fastdiv((uint32_t)sc_max), make_fastdiv((uint32_t)(rest ? rest : sc_max))};
+}
+
 // Everything a kernel needs to address one problem. Sizes are validated on
 // the host (every element count below 2^31 except where noted).
 struct Geometry {
@@ -35,6 +71,7 @@ struct Geometry {
     int32_t units;         // B * N_h * N_q * chunks
     int32_t blocks;        // grid size
     Levels lv;
+    FastDiv nq_div, nh_div, np_div, ch_div;  // by N_q, N_h, N_p, chunks
 };
 
 // Destination-tiled grad_value pass (backward). Every level is cut into
@@ -96,6 +133,19 @@ __device__ __forceinline__ void level_of(const Levels& lv, int l, int& H, int& W
     for (int k = 0; k < kMaxLevels; ++k) {
         if (k == l) { H = lv.H[k]; W = lv.W[k]; start = lv.start[k]; }
     }
+}
+
+// The level table in LDS, one int4 (H, W, start, 0) per level, so per-thread
+// lookups by a divergent level index are one LDS read. Every thread of the
+// workgroup must call fill_level_table; it ends with a barrier.
+__device__ __forceinline__ void fill_level_table(const Levels& lv, int4* s_lv)
+{
+    if (threadIdx.x < kMaxLevels) {
+        int H, W, start;
+        level_of(lv, threadIdx.x, H, W, start);
+        s_lv[threadIdx.x] = make_int4(H, W, start, 0);
+    }
+    __syncthreads();
 }
 
 // Normalised -> pixel coordinate along an axis of `size` pixels, in float32:

@@ -28,7 +28,7 @@
 namespace msda {
 
 template <typename T, int VEC, bool BUF>
-__global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max, int64_t value_bytes,
+__global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max, ChunkDiv cdiv, int64_t value_bytes,
                                                          const T* __restrict__ value,
                                                          const float* __restrict__ loc,
                                                          const float* __restrict__ attn,
@@ -39,6 +39,8 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
     const int upb = kBlock >> lpu_log2;
     const int row = sc_max + 1;  // padded LDS row (one row per unit) against bank conflicts
     FwdRecord* s_rec = reinterpret_cast<FwdRecord*>(smem);
+    __shared__ int4 s_lv[kMaxLevels];
+    fill_level_table(g.lv, s_lv);
 
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
@@ -52,10 +54,12 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
     const int u = u0 + grp;
     int b = 0, h = 0, q = 0, chunk = 0;
     {
-        int t = u;
-        chunk = t % g.chunks; t /= g.chunks;
-        q = t % g.Nq; t /= g.Nq;
-        h = t % g.Nh; b = t / g.Nh;
+        int t = fdiv(u, g.ch_div);
+        chunk = u - t * g.chunks;
+        const int t2 = fdiv(t, g.nq_div);
+        q = t - t2 * g.Nq;
+        b = fdiv(t2, g.nh_div);
+        h = t2 - b * g.Nh;
     }
     const int c0 = ((chunk << lpu_log2) + lig) * VEC;
     const bool active = (u < g.units) && (c0 < g.Ch);
@@ -69,20 +73,21 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
         const int sc = min(sc_max, S - s0);
         if (s0 > 0) __syncthreads();
         // ---- stage: one thread per (unit, sample) of this chunk ----
+        const FastDiv& scd = cdiv.of(sc, sc_max);
         for (int i = tid; i < upb * sc; i += kBlock) {
-            const int gi = i / sc;
+            const int gi = fdiv(i, scd);
             const int s = i - gi * sc;
             const int uu = u0 + gi;
             FwdRecord rec = {make_float4(0.f, 0.f, 0.f, 0.f),
                              make_int4(no_corner<T>(), no_corner<T>(), no_corner<T>(), no_corner<T>())};
             if (uu < g.units) {
-                int t = uu / g.chunks;
-                const int qq = t % g.Nq; t /= g.Nq;
-                const int hh = t % g.Nh, bb = t / g.Nh;
+                const int t = fdiv(uu, g.ch_div);
+                const int t2 = fdiv(t, g.nq_div);
+                const int qq = t - t2 * g.Nq;
+                const int bb = fdiv(t2, g.nh_div), hh = t2 - bb * g.Nh;
                 const int si = s0 + s;
-                const int l = si / g.Np;
-                int H, W, start;
-                level_of(g.lv, l, H, W, start);
+                const int4 lvl = s_lv[fdiv(si, g.np_div)];
+                const int H = lvl.x, W = lvl.y, start = lvl.z;
                 const int idx = ((bb * g.Nq + qq) * g.Nh + hh) * S + si;
                 float ux, uy;
                 if (g.b2q) {
@@ -118,11 +123,12 @@ static hipError_t launch_forward_t(const Geometry& g, int64_t value_bytes, const
     int sc = g.S < 16 ? g.S : 16;
     while (sc > 1 && (size_t)upb * (sc + 1) * rec > kLdsBudget) --sc;
     const size_t lds = (size_t)upb * (sc + 1) * rec;
+    const ChunkDiv cdiv = make_chunkdiv(g.S, sc);
     if (buffer_loads_ok(value_bytes))
-        hipLaunchKernelGGL((forward_kernel<T, VEC, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+        hipLaunchKernelGGL((forward_kernel<T, VEC, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc, cdiv,
                            value_bytes, static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
     else
-        hipLaunchKernelGGL((forward_kernel<T, VEC, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+        hipLaunchKernelGGL((forward_kernel<T, VEC, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc, cdiv,
                            value_bytes, static_cast<const T*>(value), loc, attn, static_cast<T*>(out));
     return hipGetLastError();
 }
