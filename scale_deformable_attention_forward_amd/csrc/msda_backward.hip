@@ -666,7 +666,7 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 // (kRectCols + 1) anchor bins around it and loads each entry's grad_output
 // row once per bin, adding it to every pixel of the rectangle it reaches
 // (15 row loads per 8 pixels instead of 32 with one pixel per owner).
-template <typename T, int LPU>
+template <typename T, int LPU, bool BUF>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
     float* __restrict__ partial, int accumulate)
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
-    __shared__ float4 s_ent[E];              // (fx, fy, A, q)
+    __shared__ float4 s_ent[E];              // (A (1 - fy), A fy, fx, element offset q * N_h * C_h of the grad_output row)
     __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
     __shared__ uint32_t s_bkey[E];           // keys in binned order
     __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
@@ -708,6 +708,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
+    // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
+    const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, BUF ? (int64_t)g.Nq * gq * (int64_t)sizeof(T) : 0);
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
@@ -758,8 +760,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             int x0, y0;
             unpack_anchor(__float_as_uint(rc.x), x0, y0);
             const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            const int q = (int)k / g.Np;
-            s_ent[i] = make_float4(rc.y, rc.z, rc.w, __int_as_float(q));
+            const int q = fdiv((int)k, g.np_div);
+            const float fx = rc.y, fy = rc.z, A = rc.w;
+            s_ent[i] = make_float4(A * (1.f - fy), A * fy, fx, __int_as_float(q * gq));
             s_key[i] = k;
             s_bin_of[i] = (uint16_t)bin;
             atomicAdd(&s_cursor[bin], 1);
@@ -827,14 +830,15 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                         float gv[4][4];
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            ent[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                            float t4[4] = {0.f, 0.f, 0.f, 0.f};
-                            if (e + u < e1) {
-                                ent[u] = s_ent[s_sorted[e + u]];
-                                VecIO<T, 4>::load(gl + __float_as_int(ent[u].w) * gq, t4);
-                            }
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) gv[u][i] = t4[i];
+                            // past the bin's end: repeat its last entry with zero weight
+                            const bool ok = e + u < e1;
+                            ent[u] = s_ent[s_sorted[ok ? e + u : e1 - 1]];
+                            if (!ok) ent[u].x = ent[u].y = 0.f;
+                            if constexpr (BUF)
+                                BufIO<T, 4>::load(gr, (uint32_t)(__float_as_int(ent[u].w) + ch) * (uint32_t)sizeof(T),
+                                                  gv[u]);
+                            else
+                                VecIO<T, 4>::load(gl + __float_as_int(ent[u].w), gv[u]);
                         }
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
@@ -844,12 +848,12 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                             for (int dy = 0; dy < 2; ++dy) {
                                 const int pr = bi - 1 + dy;
                                 if (pr < 0 || pr >= RH) continue;
-                                const float wy = ent[u].z * (dy ? ent[u].y : 1.f - ent[u].y);
+                                const float wy = dy ? ent[u].y : ent[u].x;
 #pragma unroll
                                 for (int dx = 0; dx < 2; ++dx) {
                                     const int pc = bj - 1 + dx;
                                     if (pc < 0 || pc >= RW) continue;
-                                    const float coef = wy * (dx ? ent[u].x : 1.f - ent[u].x);
+                                    const float coef = wy * (dx ? ent[u].z : 1.f - ent[u].z);
                                     bs[dy][dx].x = __builtin_fmaf(coef, gv[u][0], bs[dy][dx].x);
                                     bs[dy][dx].y = __builtin_fmaf(coef, gv[u][1], bs[dy][dx].y);
                                     bs[dy][dx].z = __builtin_fmaf(coef, gv[u][2], bs[dy][dx].z);
@@ -1097,8 +1101,14 @@ static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w
                                  void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
-    hipLaunchKernelGGL((tile_scatter_kernel<T, LPU>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g, tp,
-                       w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
+    const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
+    if (buffer_loads_ok(slab_rows_bytes))
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g,
+                           tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
+    else
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
+                           g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial,
+                           accumulate);
     if (tp.rpieces > 0)
         hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
                            0, stream, g, tp, partial, static_cast<T*>(grad_value), accumulate);
