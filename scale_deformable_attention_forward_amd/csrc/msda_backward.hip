@@ -678,9 +678,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
     __shared__ uint32_t s_bkey[E];           // keys in binned order
     __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
-    __shared__ uint16_t s_binned[E];         // staged entries grouped by bin (any order inside)
-    __shared__ uint16_t s_sorted[E];         // staged entries ordered by (bin, k)
-    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_sorted
+    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_ent once it is sorted by (bin, k)
     __shared__ int s_cursor[kTileBins];
     __shared__ int s_wave[kWaves];
 
@@ -738,9 +736,11 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         // stage a pass of list entries and count them per anchor bin
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
+        // (the entries' sample indices stay in registers until the entries are
+        // written to LDS in their sorted place)
         constexpr int kStage = kTileEntries / kTileBlock;
         uint32_t kk[kStage];
-        float4 rcs[kStage];
+        uint32_t an[kStage];
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
@@ -749,21 +749,16 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
-            rcs[u] = i < m_cnt ? srec[kk[u]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            an[u] = i < m_cnt ? reinterpret_cast<const uint32_t*>(srec + kk[u])[0] : 0u;  // anchor bits
         }
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
             if (i >= m_cnt) continue;
-            const uint32_t k = kk[u];
-            const float4 rc = rcs[u];
             int x0, y0;
-            unpack_anchor(__float_as_uint(rc.x), x0, y0);
+            unpack_anchor(an[u], x0, y0);
             const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            const int q = fdiv((int)k, g.np_div);
-            const float fx = rc.y, fy = rc.z, A = rc.w;
-            s_ent[i] = make_float4(A * (1.f - fy), A * fy, fx, __int_as_float(q * gq));
-            s_key[i] = k;
+            s_key[i] = kk[u];
             s_bin_of[i] = (uint16_t)bin;
             atomicAdd(&s_cursor[bin], 1);
         }
@@ -795,18 +790,26 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         __syncthreads();
         for (int i = tid; i < m_cnt; i += kTileBlock) {
             const int slot = atomicAdd(&s_cursor[s_bin_of[i]], 1);
-            s_binned[slot] = (uint16_t)i;
             s_bkey[slot] = s_key[i];
         }
         __syncthreads();
         // rank every entry among its bin by k (keys are unique within a band list)
-        for (int i = tid; i < m_cnt; i += kTileBlock) {
+        // and move the entries into (bin, k) order, through registers
+        // and write each entry, from its 16-byte record (an L2 hit by now), to
+        // its place in (bin, k) order
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            if (i >= m_cnt) continue;
+            const float4 rc = srec[kk[u]];
             const int bin = s_bin_of[i];
-            const uint32_t key = s_key[i];
+            const uint32_t key = kk[u];
             const int b0 = s_bstart[bin], b1 = s_bstart[bin + 1];
             int rank = 0;
             for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
-            s_sorted[b0 + rank] = (uint16_t)i;
+            const int q = fdiv((int)key, g.np_div);
+            const float fx = rc.y, fy = rc.z, A = rc.w;
+            s_ent[b0 + rank] = make_float4(A * (1.f - fy), A * fy, fx, __int_as_float(q * gq));
         }
         __syncthreads();
         // every group walks the bins around its rectangle
@@ -832,7 +835,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                         for (int u = 0; u < 4; ++u) {
                             // past the bin's end: repeat its last entry with zero weight
                             const bool ok = e + u < e1;
-                            ent[u] = s_ent[s_sorted[ok ? e + u : e1 - 1]];
+                            ent[u] = s_ent[ok ? e + u : e1 - 1];
                             if (!ok) ent[u].x = ent[u].y = 0.f;
                             if constexpr (BUF)
                                 BufIO<T, 4>::load(gr, (uint32_t)(__float_as_int(ent[u].w) + ch) * (uint32_t)sizeof(T),
