@@ -194,6 +194,8 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         tp->part_off[l] = (int32_t)part;
         tp->rpiece_begin[l] = (int32_t)pieces;
         tp->rpieces_per_band[l] = 1;
+        tp->rows_div[l] = msda::make_fastdiv(1);
+        tp->cols_div[l] = msda::make_fastdiv(1);
         if (l >= p.N_l) {
             tp->rows[l] = tp->row_bands[l] = tp->cols[l] = tp->col_bands[l] = tp->chunks[l] = 1;
             continue;
@@ -220,6 +222,8 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         int64_t chunks = (expect + 2 * msda::kTileEntries - 1) / (2 * msda::kTileEntries);
         chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, std::min<int64_t>(nwg, 1024)));  // >= 1 run each
         tp->rows[l] = (int32_t)rows;
+        tp->rows_div[l] = msda::make_fastdiv((uint32_t)rows);
+        tp->cols_div[l] = msda::make_fastdiv((uint32_t)cols);
         tp->row_bands[l] = (int32_t)rb;
         tp->cols[l] = (int32_t)cols;
         tp->col_bands[l] = (int32_t)cb;

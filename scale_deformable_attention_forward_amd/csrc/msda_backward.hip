@@ -415,12 +415,13 @@ struct BandWs {
 
 struct LevelTiles {
     int H, W, start, R, CW, nbr, nbc, nch, band0, job0, part;
+    FastDiv rd, cd;  // by R, by CW
 };
 
 // Tile geometry of level l (static indices only, so the plan stays in kernel-argument memory).
 __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TilePlan& tp, int l)
 {
-    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0};
+    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, make_fastdiv(1), make_fastdiv(1)};
 #pragma unroll
     for (int k = 0; k < kMaxLevels; ++k) {
         if (k == l) {
@@ -435,6 +436,8 @@ __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TileP
             t.band0 = tp.band_begin[k];
             t.job0 = tp.job_begin[k];
             t.part = tp.part_off[k];
+            t.rd = tp.rows_div[k];
+            t.cd = tp.cols_div[k];
         }
     }
     return t;
@@ -445,14 +448,14 @@ __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TileP
 __device__ __forceinline__ int sample_bands(const LevelTiles& t, int x0, int y0, int (&out)[4])
 {
     int rb[2], cb[2], nr = 0, nc = 0;
-    if (y0 >= 0 && y0 < t.H) rb[nr++] = y0 / t.R;
+    if (y0 >= 0 && y0 < t.H) rb[nr++] = fdiv(y0, t.rd);
     if (y0 + 1 >= 0 && y0 + 1 < t.H) {
-        const int r = (y0 + 1) / t.R;
+        const int r = fdiv(y0 + 1, t.rd);
         if (nr == 0 || rb[0] != r) rb[nr++] = r;
     }
-    if (x0 >= 0 && x0 < t.W) cb[nc++] = x0 / t.CW;
+    if (x0 >= 0 && x0 < t.W) cb[nc++] = fdiv(x0, t.cd);
     if (x0 + 1 >= 0 && x0 + 1 < t.W) {
-        const int c = (x0 + 1) / t.CW;
+        const int c = fdiv(x0 + 1, t.cd);
         if (nc == 0 || cb[0] != c) cb[nc++] = c;
     }
     int n = 0;

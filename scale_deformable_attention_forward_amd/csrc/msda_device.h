@@ -111,6 +111,8 @@ struct TilePlan {
     int32_t part_off[kMaxLevels];        // first partial-tile float of level l within the slab
     int32_t rpieces_per_band[kMaxLevels];
     int32_t rpiece_begin[kMaxLevels + 1];
+    FastDiv rows_div[kMaxLevels];        // by rows[l]
+    FastDiv cols_div[kMaxLevels];        // by cols[l]
 };
 
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).
