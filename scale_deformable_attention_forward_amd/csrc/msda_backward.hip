@@ -941,9 +941,25 @@ __global__ __launch_bounds__(kBlock) void band_reduce_kernel(Geometry g, TilePla
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
     for (int i = i0 + (int)threadIdx.x; i < i1; i += kBlock) {
-        float4 s = reinterpret_cast<const float4*>(slot0)[i];
-        for (int c = 1; c < t.nch; ++c) {
-            const float4 v = reinterpret_cast<const float4*>(slot0 + c * tile)[i];
+        const float4* part = reinterpret_cast<const float4*>(slot0) + i;
+        const size_t step = tile / 4;  // float4s between consecutive chunks' tiles
+        float4 s = part[0];
+        int c = 1;
+        // eight chunks' loads in flight at a time; the sum still runs in chunk order
+        for (; c + 8 <= t.nch; c += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = part[(size_t)(c + j) * step];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s.x += v[j].x;
+                s.y += v[j].y;
+                s.z += v[j].z;
+                s.w += v[j].w;
+            }
+        }
+        for (; c < t.nch; ++c) {
+            const float4 v = part[(size_t)c * step];
             s.x += v.x;
             s.y += v.y;
             s.z += v.z;
