@@ -677,7 +677,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
-    __shared__ float4 s_ent[E];              // (A (1 - fy), A fy, fx, element offset q * N_h * C_h of the grad_output row)
+    __shared__ float4 s_ent[E + 1];          // (A (1 - fy), A fy, fx, element offset q * N_h * C_h of the grad_output row);
+                                             // s_ent[E]: a zero-weight entry
     __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
     __shared__ uint32_t s_bkey[E];           // keys in binned order
     __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
@@ -725,6 +726,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     for (int i = 0; i < RH; ++i)
 #pragma unroll
         for (int j = 0; j < RW; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid == 0) s_ent[E] = make_float4(0.f, 0.f, 0.f, 0.f);  // read only after the passes' barriers
 
     // A pass stages whole runs (at most E entries; one run never exceeds
     // kBandChunk <= E), so which entries share a pass does not depend on the
@@ -796,9 +798,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             s_bkey[slot] = s_key[i];
         }
         __syncthreads();
-        // rank every entry among its bin by k (keys are unique within a band list)
-        // and move the entries into (bin, k) order, through registers
-        // and write each entry, from its 16-byte record (an L2 hit by now), to
+        // rank every entry among its bin by k (keys are unique within a band
+        // list) and write it, from its 16-byte record (an L2 hit by now), to
         // its place in (bin, k) order
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
@@ -836,10 +837,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                         float gv[4][4];
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            // past the bin's end: repeat its last entry with zero weight
-                            const bool ok = e + u < e1;
-                            ent[u] = s_ent[ok ? e + u : e1 - 1];
-                            if (!ok) ent[u].x = ent[u].y = 0.f;
+                            // past the bin's end: the zero-weight entry
+                            ent[u] = s_ent[e + u < e1 ? e + u : E];
                             if constexpr (BUF)
                                 BufIO<T, 4>::load(gr, (uint32_t)(__float_as_int(ent[u].w) + ch) * (uint32_t)sizeof(T),
                                                   gv[u]);
