@@ -201,12 +201,14 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
             continue;
         }
         const int64_t H = p.spatial_shapes[2 * l], W = p.spatial_shapes[2 * l + 1];
+        // a band of r x c pixels has (r + 1) x (c + 1) anchor bins, dealt out
+        // to ny x nx lane groups in blocks of RH x RW bins
         int64_t rows = 0, cols = 0, rb = 0, cb = 0;
-        const int64_t nx_max = std::min<int64_t>(groups, (W + RW - 1) / RW);
+        const int64_t nx_max = std::min<int64_t>(groups, W / RW + 1);
         for (int64_t nx = 1; nx <= nx_max; ++nx) {
-            const int64_t ny = std::min<int64_t>(groups / nx, (H + RH - 1) / RH);
-            const int64_t r = std::min<int64_t>(H, ny * RH), c = std::min<int64_t>(W, nx * RW);
-            if ((r + 1) * (c + 1) > msda::kTileBins) continue;
+            const int64_t ny = std::min<int64_t>(groups / nx, H / RH + 1);
+            const int64_t r = std::min<int64_t>(H, ny * RH - 1), c = std::min<int64_t>(W, nx * RW - 1);
+            if (r < 1 || c < 1 || (r + 1) * (c + 1) > msda::kTileBins) continue;
             const int64_t nrb = (H + r - 1) / r, ncb = (W + c - 1) / c;
             if (rows == 0 || nrb * ncb < rb * cb || (nrb * ncb == rb * cb && ncb < cb)) {
                 rows = r;

@@ -662,13 +662,20 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
     VecIO<T, 4>::store(dst, v);
 }
 
-// Tile kernel. LPU lanes per lane group (4 channels per lane); each of the
-// kTileBlock / LPU groups owns a rectangle of kRectRows x kRectCols pixels of
-// the band. The entries anchored at a corner (x0, y0) reach the 2x2 pixels
-// (x0..x0+1, y0..y0+1), so a rectangle reads the (kRectRows + 1) x
-// (kRectCols + 1) anchor bins around it and loads each entry's grad_output
-// row once per bin, adding it to every pixel of the rectangle it reaches
-// (15 row loads per 8 pixels instead of 32 with one pixel per owner).
+// Tile kernel. LPU lanes per lane group (4 channels per lane). The band's
+// anchor bins (anchor rows r0-1..r1-1, columns c0-1..c1-1) are dealt out to
+// the kTileBlock / LPU groups in blocks of kRectRows x kRectCols bins. An
+// entry anchored at (x0, y0) reaches the pixels (x0..x0+1, y0..y0+1), so a
+// group's block of bins reaches (kRectRows + 1) x (kRectCols + 1) pixels:
+// its own kRectRows x kRectCols and a halo row above and column to the left,
+// which belong to the neighbouring groups. Every entry's grad_output row is
+// thus loaded once and applied to all four corners; after the walk the
+// groups hand their halos to their neighbours through LDS, which add them in
+// a fixed order.
+// Byte offset past the end of every grad_output buffer the tile kernel reads
+// (buffer spans stay below 2^31 bytes): such a load returns zeros.
+constexpr uint32_t kNoRowBytes = 1u << 31;
+
 template <typename T, int LPU, bool BUF>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
@@ -677,12 +684,13 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
-    __shared__ float4 s_ent[E + 1];          // (A (1 - fy), A fy, fx, element offset q * N_h * C_h of the grad_output row);
-                                             // s_ent[E]: a zero-weight entry
-    __shared__ uint32_t s_key[E];            // sample index k: orders the entries of a bin
-    __shared__ uint32_t s_bkey[E];           // keys in binned order
-    __shared__ uint16_t s_bin_of[E];         // anchor bin of each staged entry
-    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_ent once it is sorted by (bin, k)
+    // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
+    // A fy (1-fx), A fy fx and the element offset q * N_h * C_h of the
+    // grad_output row; the three slots after a pass's last entry hold zeros
+    __shared__ float4 s_w[E + 3];
+    __shared__ uint32_t s_row[E + 3];
+    __shared__ uint32_t s_bkey[E];           // sample indices k in binned order
+    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_w / s_row
     __shared__ int s_cursor[kTileBins];
     __shared__ int s_wave[kWaves];
 
@@ -715,18 +723,19 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
-    const int rects_x = (tw + RW - 1) / RW;
-    const int gy = grp / rects_x, gx = grp - gy * rects_x;
-    const int ry = gy * RH, rx = gx * RW;    // the group's rectangle, band-local
-    const bool grp_ok = ch < g.Ch && ry < th;
+    const int gnx = (tw + RW) / RW, gny = (th + RH) / RH;  // group blocks cover the (th+1) x (tw+1) bins
+    const int gy = grp / gnx, gx = grp - gy * gnx;
+    const int by0 = gy * RH, bx0 = gx * RW;  // the group's first bin (bin row 0 is anchor row r0 - 1)
+    const bool grp_ok = ch < g.Ch && gy < gny;
     const T* gl = grow0 + ch;
 
-    float4 acc[RH][RW];
+    // acc[a][c] is band-local pixel (by0 - 1 + a, bx0 - 1 + c): rows and
+    // columns 1.. are the group's own, row 0 and column 0 its halo
+    float4 acc[RH + 1][RW + 1];
 #pragma unroll
-    for (int i = 0; i < RH; ++i)
+    for (int i = 0; i <= RH; ++i)
 #pragma unroll
-        for (int j = 0; j < RW; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid == 0) s_ent[E] = make_float4(0.f, 0.f, 0.f, 0.f);  // read only after the passes' barriers
+        for (int j = 0; j <= RW; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
 
     // A pass stages whole runs (at most E entries; one run never exceeds
     // kBandChunk <= E), so which entries share a pass does not depend on the
@@ -741,11 +750,12 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         // stage a pass of list entries and count them per anchor bin
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
-        // (the entries' sample indices stay in registers until the entries are
-        // written to LDS in their sorted place)
+        // (each thread keeps its entries' sample indices and bins in registers
+        // until it writes them to LDS in their sorted place)
         constexpr int kStage = kTileEntries / kTileBlock;
         uint32_t kk[kStage];
         uint32_t an[kStage];
+        int bn[kStage];
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
@@ -762,10 +772,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             if (i >= m_cnt) continue;
             int x0, y0;
             unpack_anchor(an[u], x0, y0);
-            const int bin = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            s_key[i] = kk[u];
-            s_bin_of[i] = (uint16_t)bin;
-            atomicAdd(&s_cursor[bin], 1);
+            bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
+            atomicAdd(&s_cursor[bn[u]], 1);
         }
         __syncthreads();
         // exclusive scan of the bin counts
@@ -793,10 +801,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         }
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
         __syncthreads();
-        for (int i = tid; i < m_cnt; i += kTileBlock) {
-            const int slot = atomicAdd(&s_cursor[s_bin_of[i]], 1);
-            s_bkey[slot] = s_key[i];
-        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u)
+            if (tid + u * kTileBlock < m_cnt) s_bkey[atomicAdd(&s_cursor[bn[u]], 1)] = kk[u];
         __syncthreads();
         // rank every entry among its bin by k (keys are unique within a band
         // list) and write it, from its 16-byte record (an L2 hit by now), to
@@ -806,79 +813,105 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             const int i = tid + u * kTileBlock;
             if (i >= m_cnt) continue;
             const float4 rc = srec[kk[u]];
-            const int bin = s_bin_of[i];
             const uint32_t key = kk[u];
-            const int b0 = s_bstart[bin], b1 = s_bstart[bin + 1];
+            const int b0 = s_bstart[bn[u]], b1 = s_bstart[bn[u] + 1];
             int rank = 0;
             for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
             const int q = fdiv((int)key, g.np_div);
             const float fx = rc.y, fy = rc.z, A = rc.w;
-            s_ent[b0 + rank] = make_float4(A * (1.f - fy), A * fy, fx, __int_as_float(q * gq));
+            const float a0 = A * (1.f - fy), a1 = A * fy;
+            s_w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
+            s_row[b0 + rank] = (uint32_t)(q * gq);
+        }
+        if (tid < 3) {
+            s_w[m_cnt + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+            s_row[m_cnt + tid] = 0u;
         }
         __syncthreads();
         // every group walks the bins around its rectangle
         if (grp_ok) {
+            // terms of four entries of the group's bin (bi, bj): corner (dx, dy)
+            // of such an entry is acc[bi + dy][bj + dx]; the four terms are
+            // summed before they join the pixel's total, which keeps float32
+            // rounding chains short
+            auto add_terms = [&](int bi, int bj, const float4 (&wv)[4], const float (&gv)[4][4]) {
 #pragma unroll
-            for (int bi = 0; bi <= RH; ++bi) {
+                for (int dy = 0; dy < 2; ++dy) {
+                    const int pr = bi + dy;
 #pragma unroll
-                for (int bj = 0; bj <= RW; ++bj) {
-                    const int by = ry + bi, bx = rx + bj;
-                    if (by > th || bx > tw) continue;  // no such bin
-                    const int bin = by * nbw + bx;
-                    const int e1 = s_bstart[bin + 1];
-                    // per-bin partial sums keep float32 rounding chains short
-                    float4 bs[2][2];
-#pragma unroll
-                    for (int dy = 0; dy < 2; ++dy)
-#pragma unroll
-                        for (int dx = 0; dx < 2; ++dx) bs[dy][dx] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    for (int e = s_bstart[bin]; e < e1; e += 4) {
-                        float4 ent[4];
-                        float gv[4][4];
+                    for (int dx = 0; dx < 2; ++dx) {
+                        const int pc = bj + dx;
+                        float4 ts;
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            // past the bin's end: the zero-weight entry
-                            ent[u] = s_ent[e + u < e1 ? e + u : E];
-                            if constexpr (BUF)
-                                BufIO<T, 4>::load(gr, (uint32_t)(__float_as_int(ent[u].w) + ch) * (uint32_t)sizeof(T),
-                                                  gv[u]);
-                            else
-                                VecIO<T, 4>::load(gl + __float_as_int(ent[u].w), gv[u]);
-                        }
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            // corner (dx, dy) of an entry in bin (bi, bj) is pixel
-                            // (bi - 1 + dy, bj - 1 + dx) of the rectangle
-#pragma unroll
-                            for (int dy = 0; dy < 2; ++dy) {
-                                const int pr = bi - 1 + dy;
-                                if (pr < 0 || pr >= RH) continue;
-                                const float wy = dy ? ent[u].y : ent[u].x;
-#pragma unroll
-                                for (int dx = 0; dx < 2; ++dx) {
-                                    const int pc = bj - 1 + dx;
-                                    if (pc < 0 || pc >= RW) continue;
-                                    const float coef = wy * (dx ? ent[u].z : 1.f - ent[u].z);
-                                    bs[dy][dx].x = __builtin_fmaf(coef, gv[u][0], bs[dy][dx].x);
-                                    bs[dy][dx].y = __builtin_fmaf(coef, gv[u][1], bs[dy][dx].y);
-                                    bs[dy][dx].z = __builtin_fmaf(coef, gv[u][2], bs[dy][dx].z);
-                                    bs[dy][dx].w = __builtin_fmaf(coef, gv[u][3], bs[dy][dx].w);
-                                }
+                            const float4 w4 = wv[u];
+                            const float wc = dy ? (dx ? w4.w : w4.z) : (dx ? w4.y : w4.x);
+                            if (u == 0) {
+                                ts = make_float4(wc * gv[u][0], wc * gv[u][1], wc * gv[u][2], wc * gv[u][3]);
+                            } else {
+                                ts.x = __builtin_fmaf(wc, gv[u][0], ts.x);
+                                ts.y = __builtin_fmaf(wc, gv[u][1], ts.y);
+                                ts.z = __builtin_fmaf(wc, gv[u][2], ts.z);
+                                ts.w = __builtin_fmaf(wc, gv[u][3], ts.w);
                             }
                         }
+                        acc[pr][pc].x += ts.x;
+                        acc[pr][pc].y += ts.y;
+                        acc[pr][pc].z += ts.z;
+                        acc[pr][pc].w += ts.w;
                     }
+                }
+            };
+            // entry range [b0, b1) of the group's bin (bi, bj); empty where there is no such bin
+            auto bin_range = [&](int bi, int bj, int& b0, int& b1) {
+                const int by = by0 + bi, bx = bx0 + bj;
+                b0 = b1 = 0;
+                if (by > th || bx > tw) return;
+                const int bin = by * nbw + bx;
+                b0 = s_bstart[bin];
+                b1 = s_bstart[bin + 1];
+            };
+            if constexpr (BUF) {
 #pragma unroll
-                    for (int dy = 0; dy < 2; ++dy) {
-                        const int pr = bi - 1 + dy;
-                        if (pr < 0 || pr >= RH) continue;
+                for (int bi = 0; bi < RH; ++bi) {
 #pragma unroll
-                        for (int dx = 0; dx < 2; ++dx) {
-                            const int pc = bj - 1 + dx;
-                            if (pc < 0 || pc >= RW) continue;
-                            acc[pr][pc].x += bs[dy][dx].x;
-                            acc[pr][pc].y += bs[dy][dx].y;
-                            acc[pr][pc].z += bs[dy][dx].z;
-                            acc[pr][pc].w += bs[dy][dx].w;
+                    for (int bj = 0; bj < RW; ++bj) {
+                        int e0, e1;
+                        bin_range(bi, bj, e0, e1);
+                        for (int e = e0; e < e1; e += 4) {
+                            float4 wv[4];
+                            float gv[4][4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                // slots past the bin's end load no row (the buffer
+                                // returns zeros past its end), so whatever
+                                // weights they read add nothing
+                                wv[u] = s_w[e + u];
+                                const uint32_t row = s_row[e + u];
+                                BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
+                            }
+                            add_terms(bi, bj, wv, gv);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int bi = 0; bi < RH; ++bi) {
+#pragma unroll
+                    for (int bj = 0; bj < RW; ++bj) {
+                        int e0, e1;
+                        bin_range(bi, bj, e0, e1);
+                        for (int e = e0; e < e1; e += 4) {
+                            float4 wv[4];
+                            float gv[4][4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                // slots past the bin's end read a zero-weight slot
+                                const int ei = e + u < e1 ? e + u : m_cnt;
+                                wv[u] = s_w[ei];
+                                VecIO<T, 4>::load(gl + s_row[ei], gv[u]);
+                            }
+                            add_terms(bi, bj, wv, gv);
                         }
                     }
                 }
@@ -887,17 +920,66 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         __syncthreads();
     }
 
+    // halo exchange through LDS (s_w is free now): the halo row goes to the
+    // group above, the halo column to the group on the left and the corner to
+    // the group above-left; a pixel adds its own sum, then the values from
+    // below, from the right and from below-right, in that order
+    static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s_w");
+    float4* s_x = s_w;
+    if (grp_ok) {
+#pragma unroll
+        for (int c = 1; c <= RW; ++c) s_x[(c - 1) * kTileBlock + tid] = acc[0][c];
+    }
+    __syncthreads();
+    if (grp_ok && gy + 1 < gny) {
+#pragma unroll
+        for (int c = 1; c <= RW; ++c) {
+            const float4 v = s_x[(c - 1) * kTileBlock + tid + gnx * LPU];
+            acc[RH][c].x += v.x;
+            acc[RH][c].y += v.y;
+            acc[RH][c].z += v.z;
+            acc[RH][c].w += v.w;
+        }
+    }
+    __syncthreads();
+    if (grp_ok) {
+#pragma unroll
+        for (int r = 1; r <= RH; ++r) s_x[(r - 1) * kTileBlock + tid] = acc[r][0];
+        s_x[RH * kTileBlock + tid] = acc[0][0];
+    }
+    __syncthreads();
     if (!grp_ok) return;
+    if (gx + 1 < gnx) {
+#pragma unroll
+        for (int r = 1; r <= RH; ++r) {
+            const float4 v = s_x[(r - 1) * kTileBlock + tid + LPU];
+            acc[r][RW].x += v.x;
+            acc[r][RW].y += v.y;
+            acc[r][RW].z += v.z;
+            acc[r][RW].w += v.w;
+        }
+        if (gy + 1 < gny) {
+            const float4 v = s_x[RH * kTileBlock + tid + (gnx + 1) * LPU];
+            acc[RH][RW].x += v.x;
+            acc[RH][RW].y += v.y;
+            acc[RH][RW].z += v.z;
+            acc[RH][RW].w += v.w;
+        }
+    }
+
+    // own pixels: band-local (by0 - 1 + i, bx0 - 1 + j) for i, j >= 1
     if (t.nch == 1) {
         // the band's only job: store the final values
         const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
         T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
 #pragma unroll
-        for (int i = 0; i < RH; ++i)
+        for (int i = 1; i <= RH; ++i)
 #pragma unroll
-            for (int j = 0; j < RW; ++j)
-                if (ry + i < th && rx + j < tw)
-                    store_grad4(out + ((r0 + ry + i) * t.W + c0 + rx + j) * pstride + ch, acc[i][j], accumulate);
+            for (int j = 1; j <= RW; ++j) {
+                const int py = by0 - 1 + i, px = bx0 - 1 + j;
+                if (py < th && px < tw)
+                    store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[i][j], accumulate);
+            }
         return;
     }
     // one chunk of a split band: its partial tile, pixel-major (band-local
@@ -905,11 +987,12 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     float* slot = partial + (size_t)slab * tp.part_per_slab + t.part +
                   (size_t)(band * t.nch + chunk) * (t.R * t.CW) * g.Ch;
 #pragma unroll
-    for (int i = 0; i < RH; ++i)
+    for (int i = 1; i <= RH; ++i)
 #pragma unroll
-        for (int j = 0; j < RW; ++j)
-            if (ry + i < th && rx + j < tw)
-                *reinterpret_cast<float4*>(slot + ((ry + i) * tw + rx + j) * g.Ch + ch) = acc[i][j];
+        for (int j = 1; j <= RW; ++j) {
+            const int py = by0 - 1 + i, px = bx0 - 1 + j;
+            if (py < th && px < tw) *reinterpret_cast<float4*>(slot + (py * tw + px) * g.Ch + ch) = acc[i][j];
+        }
 }
 
 // Adds the partial tiles of split bands in chunk order and stores grad_value.
