@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 struct BandWs {
     int* cnt;            // [slabs][bands][nwg]
     int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
-    uint32_t* k;
+    uint2* k;            // list entries: (sample index k, its anchor bits)
     const float4* rec;   // AnchorWs::rec
 };
 
@@ -623,7 +623,8 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     for (int i = tid; i < total; i += kBandBlock) {
         const int bnd = s_band[i];
         const size_t pos = lbase + run_off[(size_t)bnd * tp.nwg] + (i - loff[bnd]);
-        w.k[pos] = s_k[i];
+        // the run's anchors are 8 KB, cached by now
+        w.k[pos] = make_uint2(s_k[i], anchor[sbase + s_k[i]]);
     }
 }
 
@@ -759,12 +760,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
-            kk[u] = i < m_cnt ? w.k[lbase + p0 + i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            const int i = tid + u * kTileBlock;
-            an[u] = i < m_cnt ? reinterpret_cast<const uint32_t*>(srec + kk[u])[0] : 0u;  // anchor bits
+            const uint2 ka = i < m_cnt ? w.k[lbase + p0 + i] : make_uint2(0u, 0u);
+            kk[u] = ka.x;
+            an[u] = ka.y;
         }
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
@@ -1261,7 +1259,7 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     const size_t runs = nb * (size_t)tp.nwg;
     w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
     w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
-    w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
+    w.k = reinterpret_cast<uint2*>(take(cap * 8));
     w.rec = a.rec;
     float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
