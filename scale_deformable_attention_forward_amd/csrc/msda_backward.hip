@@ -547,91 +547,42 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
 }
 
 // Bucketing 3/3: fill the band lists. Grid as band_count_kernel. Each
-// workgroup takes its run lengths from band_count_kernel, orders its entries
-// by band in LDS and writes its run of every band at the offset the scan gave
-// it, with consecutive stores. (Order inside a run is arbitrary; the tile
-// pass orders what it sums.)
-// Dynamic LDS: 2 * (max_bands + 1) ints, then max_entries (k, band) pairs
-// (kBandChunk samples times the most bands one sample can touch).
+// workgroup writes its run of every band at the offset the scan gave it: an
+// LDS counter per band hands out the places in the run (so the order inside
+// a run is arbitrary; the tile pass orders what it sums). An entry is the
+// sample index k and its anchor bits.
+// Dynamic LDS: 2 * max_bands ints.
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
-                                                               const uint32_t* __restrict__ anchor, int max_bands,
-                                                               int max_entries)
+                                                               const uint32_t* __restrict__ anchor, int max_bands)
 {
-    constexpr int kWaves = kBandBlock / kWave;
     extern __shared__ int dyn[];
-    int* hist = dyn;
-    int* loff = hist + max_bands + 1;
-    uint32_t* s_k = reinterpret_cast<uint32_t*>(loff + max_bands + 1);
-    uint16_t* s_band = reinterpret_cast<uint16_t*>(s_k + max_entries);
-    __shared__ int s_wave[kWaves];
+    int* placed = dyn;               // entries of each band placed so far
+    int* start = placed + max_bands;  // where this run starts in each band's list
     const int tid = threadIdx.x;
     const int wg = blockIdx.x, l = blockIdx.y, slab = blockIdx.z;
     const LevelTiles t = level_tiles(g, tp, l);
     const int nb = t.nbr * t.nbc;
     const int nsamp = g.Nq * g.Np;
     const int k0 = wg * kBandChunk, k1 = min(nsamp, k0 + kBandChunk);
-    // this run's count of every band of the level, from band_count_kernel
-    const int* c = w.cnt + ((size_t)slab * tp.bands + t.band0) * tp.nwg + wg;
-    for (int i = tid; i < nb; i += kBandBlock) hist[i] = c[(size_t)i * tp.nwg];
+    const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)t.band0 * tp.nwg + wg;
+    for (int i = tid; i < nb; i += kBandBlock) {
+        placed[i] = 0;
+        start[i] = run_off[(size_t)i * tp.nwg];
+    }
     const size_t sbase = (size_t)(slab * g.Nl + l) * nsamp;
     uint32_t a[kRunPerThread];
     load_run_anchors(anchor + sbase, k0, k1, a);
     __syncthreads();
-    // exclusive scan of hist[0..nb) into loff, in rounds of kBandBlock bands
-    const int lane = tid % kWave, wave = tid / kWave;
-    int carry = 0;
-    for (int r = 0; r < nb; r += kBandBlock) {
-        const int i = r + tid;
-        const int v = i < nb ? hist[i] : 0;
-        int incl = v;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int u = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += u;
-        }
-        if (lane == kWave - 1) s_wave[wave] = incl;
-        __syncthreads();
-        int before = carry, total = carry;
-        for (int ww = 0; ww < kWaves; ++ww) {
-            before += ww < wave ? s_wave[ww] : 0;
-            total += s_wave[ww];
-        }
-        if (i < nb) loff[i] = before + incl - v;
-        carry = total;
-        __syncthreads();
-    }
-    if (tid == 0) loff[nb] = carry;
-    for (int i = tid; i < nb; i += kBandBlock) hist[i] = 0;
-    __syncthreads();
+    uint2* list = w.k + (size_t)slab * tp.cap;
 #pragma unroll
     for (int i = 0; i < kRunPerThread; ++i) {
         if (a[i] == 0xffffffffu) continue;
-        const int k = k0 + tid + i * kBandBlock;
+        const uint32_t k = (uint32_t)(k0 + tid + i * kBandBlock);
         int x0, y0, bands[4];
         unpack_anchor(a[i], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
-        for (int j = 0; j < n; ++j) {
-            const int slot = loff[bands[j]] + atomicAdd(&hist[bands[j]], 1);
-            s_k[slot] = (uint32_t)k;
-            s_band[slot] = (uint16_t)bands[j];
-        }
+        for (int j = 0; j < n; ++j) list[start[bands[j]] + atomicAdd(&placed[bands[j]], 1)] = make_uint2(k, a[i]);
     }
-    __syncthreads();
-    const int total = loff[nb];
-    const size_t lbase = (size_t)slab * tp.cap;
-    const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)t.band0 * tp.nwg + wg;
-    for (int i = tid; i < total; i += kBandBlock) {
-        const int bnd = s_band[i];
-        const size_t pos = lbase + run_off[(size_t)bnd * tp.nwg] + (i - loff[bnd]);
-        // the run's anchors are 8 KB, cached by now
-        w.k[pos] = make_uint2(s_k[i], anchor[sbase + s_k[i]]);
-    }
-}
-
-// Dynamic LDS bytes of band_fill_kernel.
-static size_t band_fill_lds(int max_bands, int max_entries)
-{
-    return (size_t)2 * (max_bands + 1) * sizeof(int) + (size_t)max_entries * (sizeof(uint32_t) + sizeof(uint16_t));
 }
 
 // Band of level-local index `band`: rows [r0, r0 + th), columns [c0, c0 + tw).
@@ -1316,20 +1267,10 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
     const dim3 bgrid(tp.nwg, g.Nl, slabs);
     hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
     hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
-    int max_bands = 1, max_mult = 2;
-    for (int l = 0; l < g.Nl; ++l) {
-        max_bands = std::max(max_bands, tp.row_bands[l] * tp.col_bands[l]);
-        if (tp.col_bands[l] > 1) max_mult = 4;
-    }
-    const int max_entries = kBandChunk * max_mult;
-    const size_t fill_lds = band_fill_lds(max_bands, max_entries);
-    if (fill_lds > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&band_fill_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)fill_lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), fill_lds, stream, g, tp, bw, ws.anchor,
-                       max_bands, max_entries);
+    int max_bands = 1;
+    for (int l = 0; l < g.Nl; ++l) max_bands = std::max(max_bands, tp.row_bands[l] * tp.col_bands[l]);
+    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), (size_t)2 * max_bands * sizeof(int), stream, g, tp,
+                       bw, ws.anchor, max_bands);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
