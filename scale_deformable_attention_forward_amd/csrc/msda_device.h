@@ -90,7 +90,7 @@ constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (
 constexpr int kBandBlock = 256;          // threads of the bucketing kernels
 constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
-constexpr int kReduceF4 = 1024;          // float4s of a band one reduction workgroup adds up
+constexpr int kReduceF4 = 256;           // float4s of a band one reduction workgroup adds up
 static_assert(kBandChunk <= kTileEntries, "one run (<= kBandChunk entries) must fit one LDS pass");
 static_assert(kBandChunk % kBandBlock == 0 && kTileEntries % kTileBlock == 0, "whole per-thread batches");
 
