@@ -514,6 +514,9 @@ __global__ __launch_bounds__(kBandBlock) void band_count_kernel(Geometry g, Tile
 }
 
 // Bucketing 2/3: exclusive prefix of the (band, run) counts of each slab.
+// Each thread scans kScanItems consecutive counts, so one block-wide scan of
+// the threads' totals covers kBlock * kScanItems counts.
+constexpr int kScanItems = 16;
 __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const int* __restrict__ cnt,
                                                            int* __restrict__ off)
 {
@@ -523,10 +526,16 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
     const int* c = cnt + (size_t)slab * n;
     int* o = off + (size_t)slab * (n + 1);
     int carry = 0;
-    for (int base = 0; base < n; base += kBlock) {
-        const int i = base + tid;
-        const int v = i < n ? c[i] : 0;
-        int incl = v;
+    for (int base = 0; base < n; base += kBlock * kScanItems) {
+        const int i0 = base + tid * kScanItems;
+        int v[kScanItems];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            v[j] = i0 + j < n ? c[i0 + j] : 0;
+            sum += v[j];
+        }
+        int incl = sum;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
             const int u = __shfl_up(incl, d, kWave);
@@ -539,7 +548,12 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
             before += w < wave ? s_wave[w] : 0;
             total += s_wave[w];
         }
-        if (i < n) o[i] = carry + before + incl - v;
+        int run = carry + before + incl - sum;
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            if (i0 + j < n) o[i0 + j] = run;
+            run += v[j];
+        }
         carry += total;
         __syncthreads();
     }
