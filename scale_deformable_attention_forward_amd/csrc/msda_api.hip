@@ -169,11 +169,12 @@ bool fast_backward_shape(const msda_problem& p)
     return true;
 }
 
-// Cut every level into bands (destination tiles) of rows x cols pixels. A
-// tile is a grid of ny x nx lane-group rectangles (kRectRows x kRectCols
-// pixels each, ny * nx <= the groups of one tile workgroup) with at most
-// kTileBins anchor bins; of those shapes the one with the fewest tiles is
-// taken (then the fewest column bands: a sample is listed once per band its
+// Cut every level into bands (destination tiles) of rows x cols pixels. The
+// (rows + 1) x (cols + 1) anchor bins of a band are dealt out to ny x nx lane
+// groups in blocks of kRectRows x kRectCols bins (ny * nx <= the groups of
+// one tile workgroup), so rows = ny * kRectRows - 1 and cols = nx *
+// kRectCols - 1 (or the level's size), with at most kTileBins anchor bins; of
+// those shapes the one with the fewest tiles is taken (then the fewest column bands: a sample is listed once per band its
 // 2x2 corner block touches). At most kMaxBandsPerLevel bands per level. A
 // band whose list is expected to hold more than two LDS passes of entries
 // (coarse levels, where many samples land on each pixel) is split into

@@ -25,9 +25,11 @@
 //     rows x cols pixels; band_count / band_scan / band_fill bucket the
 //     samples into one list per (b, h, band); tile_scatter_kernel takes one
 //     band (and, for dense coarse levels, one chunk of its list), sorts the
-//     entries by anchor corner in LDS, and each destination pixel's lane group
-//     sums A * w * G over its four neighbouring anchor bins in registers.
-//     A band of one chunk is stored directly; the chunks of a split band write
+//     entries by anchor corner in LDS, and each lane group adds A * w * G of
+//     the entries of its block of anchor bins to the four pixels each reaches,
+//     in registers, then trades the pixels of its block's rim with the
+//     neighbouring groups. A band of one chunk is stored directly; the chunks
+//     of a split band write
 //     float32 partial tiles to the workspace and band_reduce_kernel adds them
 //     in chunk order. grad_value is therefore bitwise reproducible.
 // Generic path (any C_h / alignment): backward_generic_kernel, one channel per
@@ -791,7 +793,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             s_row[m_cnt + tid] = 0u;
         }
         __syncthreads();
-        // every group walks the bins around its rectangle
+        // every group walks its block of bins
         if (grp_ok) {
             // terms of four entries of the group's bin (bi, bj): corner (dx, dy)
             // of such an entry is acc[bi + dy][bj + dx]; the four terms are

@@ -83,7 +83,7 @@ struct Geometry {
 // chunks write float32 partial tiles, which a reduction pass adds in chunk
 // order.
 constexpr int kTileBlock = 512;          // threads per tile workgroup
-constexpr int kRectRows = 2;             // a lane group owns kRectRows x kRectCols pixels
+constexpr int kRectRows = 2;             // a lane group owns kRectRows x kRectCols anchor bins
 constexpr int kRectCols = 4;
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
