@@ -84,7 +84,7 @@ struct Geometry {
 // order.
 constexpr int kTileBlock = 512;          // threads per tile workgroup
 constexpr int kRectRows = 2;             // a lane group owns kRectRows x kRectCols anchor bins
-constexpr int kRectCols = 4;
+constexpr int kRectCols = 2;
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
 constexpr int kBandBlock = 256;          // threads of the bucketing kernels
