@@ -889,48 +889,51 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // group above, the halo column to the group on the left and the corner to
     // the group above-left; a pixel adds its own sum, then the values from
     // below, from the right and from below-right, in that order
+    // (a job without entries has nothing to trade)
     static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s_w");
     float4* s_x = s_w;
-    if (grp_ok) {
+    if (run_off[w_hi] > run_off[w_lo]) {
+        if (grp_ok) {
 #pragma unroll
-        for (int c = 1; c <= RW; ++c) s_x[(c - 1) * kTileBlock + tid] = acc[0][c];
-    }
-    __syncthreads();
-    if (grp_ok && gy + 1 < gny) {
+            for (int c = 1; c <= RW; ++c) s_x[(c - 1) * kTileBlock + tid] = acc[0][c];
+        }
+        __syncthreads();
+        if (grp_ok && gy + 1 < gny) {
 #pragma unroll
-        for (int c = 1; c <= RW; ++c) {
-            const float4 v = s_x[(c - 1) * kTileBlock + tid + gnx * LPU];
-            acc[RH][c].x += v.x;
-            acc[RH][c].y += v.y;
-            acc[RH][c].z += v.z;
-            acc[RH][c].w += v.w;
+            for (int c = 1; c <= RW; ++c) {
+                const float4 v = s_x[(c - 1) * kTileBlock + tid + gnx * LPU];
+                acc[RH][c].x += v.x;
+                acc[RH][c].y += v.y;
+                acc[RH][c].z += v.z;
+                acc[RH][c].w += v.w;
+            }
+        }
+        __syncthreads();
+        if (grp_ok) {
+#pragma unroll
+            for (int r = 1; r <= RH; ++r) s_x[(r - 1) * kTileBlock + tid] = acc[r][0];
+            s_x[RH * kTileBlock + tid] = acc[0][0];
+        }
+        __syncthreads();
+        if (grp_ok && gx + 1 < gnx) {
+#pragma unroll
+            for (int r = 1; r <= RH; ++r) {
+                const float4 v = s_x[(r - 1) * kTileBlock + tid + LPU];
+                acc[r][RW].x += v.x;
+                acc[r][RW].y += v.y;
+                acc[r][RW].z += v.z;
+                acc[r][RW].w += v.w;
+            }
+            if (gy + 1 < gny) {
+                const float4 v = s_x[RH * kTileBlock + tid + (gnx + 1) * LPU];
+                acc[RH][RW].x += v.x;
+                acc[RH][RW].y += v.y;
+                acc[RH][RW].z += v.z;
+                acc[RH][RW].w += v.w;
+            }
         }
     }
-    __syncthreads();
-    if (grp_ok) {
-#pragma unroll
-        for (int r = 1; r <= RH; ++r) s_x[(r - 1) * kTileBlock + tid] = acc[r][0];
-        s_x[RH * kTileBlock + tid] = acc[0][0];
-    }
-    __syncthreads();
     if (!grp_ok) return;
-    if (gx + 1 < gnx) {
-#pragma unroll
-        for (int r = 1; r <= RH; ++r) {
-            const float4 v = s_x[(r - 1) * kTileBlock + tid + LPU];
-            acc[r][RW].x += v.x;
-            acc[r][RW].y += v.y;
-            acc[r][RW].z += v.z;
-            acc[r][RW].w += v.w;
-        }
-        if (gy + 1 < gny) {
-            const float4 v = s_x[RH * kTileBlock + tid + (gnx + 1) * LPU];
-            acc[RH][RW].x += v.x;
-            acc[RH][RW].y += v.y;
-            acc[RH][RW].z += v.z;
-            acc[RH][RW].w += v.w;
-        }
-    }
 
     // own pixels: band-local (by0 - 1 + i, bx0 - 1 + j) for i, j >= 1
     if (t.nch == 1) {
