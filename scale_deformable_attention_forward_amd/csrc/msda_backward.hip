@@ -711,8 +711,20 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // sums are therefore the same on every call.
     for (int wr = w_lo; wr < w_hi;) {
         const int p0 = run_off[wr];
+        // the pass ends before the first run that would overflow E entries;
+        // run ends never decrease, so the lanes test 64 runs per load instead
+        // of walking them one dependent load at a time
         int wn = wr + 1;
-        while (wn < w_hi && run_off[wn + 1] - p0 <= E) ++wn;
+        while (wn < w_hi) {
+            const int w = wn + tid % kWave;
+            const uint64_t fits = __ballot(w < w_hi && run_off[w + 1] - p0 <= E);
+            if (~fits == 0) {
+                wn += kWave;
+                continue;
+            }
+            wn += __ffsll((unsigned long long)~fits) - 1;
+            break;
+        }
         const int m_cnt = run_off[wn] - p0;
         wr = wn;
         // stage a pass of list entries and count them per anchor bin
