@@ -246,6 +246,14 @@ def test_split_bands_are_deterministic(dtype, gpu_device):
             RTOL[dtype])
 
 
+def test_many_runs_in_one_pass(gpu_device):
+    """160,000 samples per (b, h, level) make 79 bucketing runs; on the large
+    level every band's list is short, so one pass of the tile pass takes all
+    79 runs (more than the 64 a single ballot covers)."""
+    d = _mk(levels=((200, 200), (10, 12)), B=1, N_h=1, N_q=40000, C_h=8, N_p=4, seed=29, loc_range=(0.0, 1.0))
+    _check_backward(d, gpu_device, "many runs in one pass")
+
+
 def test_autograd_function_matches_oracle(gpu_device):
     import torch
     from scale_deformable_attention_forward_amd import ms_deformable_attention
