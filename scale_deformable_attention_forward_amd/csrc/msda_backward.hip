@@ -17,7 +17,7 @@
 //     corners, form S, dS/dx and dS/dy, reduce the three dot products with
 //     DPP, and grad_A / grad_loc leave through LDS as coalesced stores. When
 //     grad_value is wanted, the staging also writes each sample's anchor
-//     corner (x0, y0), fractions and weight to the workspace.
+//     corner (x0, y0) to the workspace.
 //  2. grad_value by destination instead of by source, so no float atomics and
 //     no order-dependent sums (global float atomics run at about one 128-byte
 //     line per request and LDS float atomics are an order of magnitude slower
@@ -178,13 +178,12 @@ __device__ __forceinline__ BwdRecord make_record(const Geometry& g, float ux, fl
     return r;
 }
 
-// Per-sample records for the destination-tiled grad_value pass, laid out
+// Per-sample anchors for the destination-tiled grad_value pass, laid out
 // [b * N_h + h][l][q][p]: the anchor corner packed (x0 + 2) | (y0 + 2) << 16
-// (x0, y0 >= -2 after the clamp above) on its own for the bucketing kernels,
-// and (anchor bits, fx, fy, A) as one 16-byte record for the tile kernel.
+// (x0, y0 >= -2 after the clamp above). The tile kernel recomputes the rest
+// of a sample's record from its location and attention weight.
 struct AnchorWs {
     uint32_t* anchor;
-    float4* rec;
 };
 
 // Stage one record per (unit, sample) of the chunk [s0, s0 + sc).
@@ -213,7 +212,6 @@ __device__ __forceinline__ void stage_records(const Geometry& g, const float* __
                 const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
                 const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
                 ws.anchor[k] = an;
-                ws.rec[k] = make_float4(__uint_as_float(an), r.fx, r.fy, a);
             }
         }
         s_rec[gi * row + s] = r;
@@ -269,7 +267,6 @@ __device__ __forceinline__ void stage_fast_records(const Geometry& g, const floa
                 const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
                 const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
                 ws.anchor[k] = an;
-                ws.rec[k] = make_float4(__uint_as_float(an), r.fx, r.fy, a);
             }
         }
         s_rec[gi * row + s] = f;
@@ -412,7 +409,6 @@ struct BandWs {
     int* cnt;            // [slabs][bands][nwg]
     int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
     uint2* k;            // list entries: (sample index k, its anchor bits)
-    const float4* rec;   // AnchorWs::rec
 };
 
 struct LevelTiles {
@@ -646,8 +642,8 @@ constexpr uint32_t kNoRowBytes = 1u << 31;
 
 template <typename T, int LPU, bool BUF>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
-    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
-    float* __restrict__ partial, int accumulate)
+    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, const float* __restrict__ loc,
+    const float* __restrict__ attn, T* __restrict__ grad_value, float* __restrict__ partial, int accumulate)
 {
     constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
@@ -683,7 +679,6 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
     const size_t lbase = (size_t)slab * tp.cap;
-    const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
     // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
@@ -783,19 +778,25 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             if (tid + u * kTileBlock < m_cnt) s_bkey[atomicAdd(&s_cursor[bn[u]], 1)] = kk[u];
         __syncthreads();
         // rank every entry among its bin by k (keys are unique within a band
-        // list) and write it, from its 16-byte record (an L2 hit by now), to
-        // its place in (bin, k) order
+        // list) and write it to its place in (bin, k) order
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
             if (i >= m_cnt) continue;
-            const float4 rc = srec[kk[u]];
             const uint32_t key = kk[u];
             const int b0 = s_bstart[bn[u]], b1 = s_bstart[bn[u] + 1];
             int rank = 0;
             for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
+            // the sample's corner weights, recomputed from its location and
+            // attention weight exactly as the backward kernel computed them
             const int q = fdiv((int)key, g.np_div);
-            const float fx = rc.y, fy = rc.z, A = rc.w;
+            const int si = l * g.Np + (int)key - q * g.Np;
+            float ux, uy;
+            read_loc(g, loc, b, q, h, si, ux, uy);
+            const float A = attn[((b * g.Nq + q) * g.Nh + h) * g.S + si];
+            int x0, y0;
+            const BwdRecord rc = make_record(g, ux, uy, A, t.H, t.W, t.start, x0, y0);
+            const float fx = rc.fx, fy = rc.fy;
             const float a0 = A * (1.f - fy), a1 = A * fy;
             s_w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
             s_row[b0 + rank] = (uint32_t)(q * gq);
@@ -1069,7 +1070,7 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const T* vslab = value + slab_off;
     float* gslab = gacc ? gacc + slab_off : nullptr;
     const T* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
-    const AnchorWs no_ws = {nullptr, nullptr};
+    const AnchorWs no_ws = {nullptr};
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
@@ -1182,16 +1183,18 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
 
 template <typename T, int LPU>
 static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
+                                 const float* loc, const float* attn,
                                  void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
     const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
     if (buffer_loads_ok(slab_rows_bytes))
         hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g,
-                           tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
+                           tp, w, static_cast<const T*>(grad_out), loc, attn, static_cast<T*>(grad_value), partial,
+                           accumulate);
     else
         hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
-                           g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial,
+                           g, tp, w, static_cast<const T*>(grad_out), loc, attn, static_cast<T*>(grad_value), partial,
                            accumulate);
     if (tp.rpieces > 0)
         hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
@@ -1236,13 +1239,11 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     };
     AnchorWs a;
     a.anchor = reinterpret_cast<uint32_t*>(take(ns * 4));
-    a.rec = reinterpret_cast<float4*>(take(ns * 16));
     BandWs w;
     const size_t runs = nb * (size_t)tp.nwg;
     w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
     w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
     w.k = reinterpret_cast<uint2*>(take(cap * 8));
-    w.rec = a.rec;
     float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
     if (bws) *bws = w;
@@ -1267,14 +1268,15 @@ static hipError_t launch_fast_typed(const Geometry& g, int lpu, const void* grad
 
 template <typename T>
 static hipError_t launch_tiles_typed(const Geometry& g, const TilePlan& tp, int lpu, BandWs w, const void* grad_out,
+                                     const float* loc, const float* attn,
                                      void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     switch (lpu) {
-    case 1: return launch_tiles_t<T, 1>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
-    case 2: return launch_tiles_t<T, 2>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
-    case 4: return launch_tiles_t<T, 4>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
-    case 8: return launch_tiles_t<T, 8>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
-    case 16: return launch_tiles_t<T, 16>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 1: return launch_tiles_t<T, 1>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    case 2: return launch_tiles_t<T, 2>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    case 4: return launch_tiles_t<T, 4>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    case 8: return launch_tiles_t<T, 8>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    case 16: return launch_tiles_t<T, 16>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1286,7 +1288,7 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                                 void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
                                 hipStream_t stream)
 {
-    AnchorWs ws = {nullptr, nullptr};
+    AnchorWs ws = {nullptr};
     BandWs bw = {};
     float* partial = nullptr;
     if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw, &partial);
@@ -1304,8 +1306,9 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                        bw, ws.anchor, max_bands);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
-                : launch_tiles_typed<float>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream);
+    return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, loc, attn, grad_value, partial, accumulate,
+                                               stream)
+                : launch_tiles_typed<float>(g, tp, lpu, bw, grad_out, loc, attn, grad_value, partial, accumulate, stream);
 }
 
 template <typename T>
