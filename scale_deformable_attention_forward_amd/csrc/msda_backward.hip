@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 struct BandWs {
     int* cnt;            // [slabs][bands][nwg]
     int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
-    uint2* k;            // list entries: (sample index k, its anchor bits)
+    uint32_t* k;         // list entries: sample indices k
 };
 
 struct LevelTiles {
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     uint32_t a[kRunPerThread];
     load_run_anchors(anchor + sbase, k0, k1, a);
     __syncthreads();
-    uint2* list = w.k + (size_t)slab * tp.cap;
+    uint32_t* list = w.k + (size_t)slab * tp.cap;
 #pragma unroll
     for (int i = 0; i < kRunPerThread; ++i) {
         if (a[i] == 0xffffffffu) continue;
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
         int x0, y0, bands[4];
         unpack_anchor(a[i], x0, y0);
         const int n = sample_bands(t, x0, y0, bands);
-        for (int j = 0; j < n; ++j) list[start[bands[j]] + atomicAdd(&placed[bands[j]], 1)] = make_uint2(k, a[i]);
+        for (int j = 0; j < n; ++j) list[start[bands[j]] + atomicAdd(&placed[bands[j]], 1)] = k;
     }
 }
 
@@ -725,25 +725,39 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         // stage a pass of list entries and count them per anchor bin
         for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
         __syncthreads();
-        // (each thread keeps its entries' sample indices and bins in registers
-        // until it writes them to LDS in their sorted place)
+        // (each thread keeps its entries' sample indices, bins and records in
+        // registers until it writes them to LDS in their sorted place)
         constexpr int kStage = kTileEntries / kTileBlock;
         uint32_t kk[kStage];
-        uint32_t an[kStage];
         int bn[kStage];
+        float rfx[kStage], rfy[kStage], ra[kStage];
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
-            const uint2 ka = i < m_cnt ? w.k[lbase + p0 + i] : make_uint2(0u, 0u);
-            kk[u] = ka.x;
-            an[u] = ka.y;
+            kk[u] = i < m_cnt ? w.k[lbase + p0 + i] : 0u;
+        }
+        // each entry's record (anchor corner, fractions, attention weight),
+        // recomputed from its location and weight exactly as the backward
+        // kernel computed it
+        float ux[kStage], uy[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int q = fdiv((int)kk[u], g.np_div);
+            const int si = l * g.Np + (int)kk[u] - q * g.Np;
+            ux[u] = uy[u] = ra[u] = 0.f;
+            if (tid + u * kTileBlock < m_cnt) {
+                read_loc(g, loc, b, q, h, si, ux[u], uy[u]);
+                ra[u] = attn[((b * g.Nq + q) * g.Nh + h) * g.S + si];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
             if (i >= m_cnt) continue;
             int x0, y0;
-            unpack_anchor(an[u], x0, y0);
+            const BwdRecord rc = make_record(g, ux[u], uy[u], ra[u], t.H, t.W, t.start, x0, y0);
+            rfx[u] = rc.fx;
+            rfy[u] = rc.fy;
             bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
             atomicAdd(&s_cursor[bn[u]], 1);
         }
@@ -787,16 +801,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             const int b0 = s_bstart[bn[u]], b1 = s_bstart[bn[u] + 1];
             int rank = 0;
             for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
-            // the sample's corner weights, recomputed from its location and
-            // attention weight exactly as the backward kernel computed them
             const int q = fdiv((int)key, g.np_div);
-            const int si = l * g.Np + (int)key - q * g.Np;
-            float ux, uy;
-            read_loc(g, loc, b, q, h, si, ux, uy);
-            const float A = attn[((b * g.Nq + q) * g.Nh + h) * g.S + si];
-            int x0, y0;
-            const BwdRecord rc = make_record(g, ux, uy, A, t.H, t.W, t.start, x0, y0);
-            const float fx = rc.fx, fy = rc.fy;
+            const float fx = rfx[u], fy = rfy[u], A = ra[u];
             const float a0 = A * (1.f - fy), a1 = A * fy;
             s_w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
             s_row[b0 + rank] = (uint32_t)(q * gq);
@@ -1243,7 +1249,7 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     const size_t runs = nb * (size_t)tp.nwg;
     w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
     w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
-    w.k = reinterpret_cast<uint2*>(take(cap * 8));
+    w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
     float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
     if (bws) *bws = w;
