@@ -229,7 +229,7 @@ struct BwdFastRecord {
 static_assert(sizeof(BwdFastRecord) == 2 * sizeof(float4), "records must tile two float4 slots");
 
 // Stage one fast-path record per (unit, sample) of the chunk [s0, s0 + sc),
-// and (with ws) the per-sample anchor and record of the grad_value pass.
+// and (with ws) the per-sample anchor of the grad_value pass.
 template <typename T>
 __device__ __forceinline__ void stage_fast_records(const Geometry& g, const float* __restrict__ loc,
                                                    const float* __restrict__ attn, BwdFastRecord* s_rec, int row,
@@ -402,9 +402,8 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 //
 // Workspace views: the per-(slab, band, run) counts and offsets, the band
 // lists (`cap` entries reserved per slab; an entry is the sample index
-// k = q * N_p + p within its (slab, level)) and the per-sample records the
-// entries point at. Run w of a band holds that band's samples among k in
-// [w * kBandChunk, (w + 1) * kBandChunk).
+// k = q * N_p + p within its (slab, level)). Run w of a band holds that
+// band's samples among k in [w * kBandChunk, (w + 1) * kBandChunk).
 struct BandWs {
     int* cnt;            // [slabs][bands][nwg]
     int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
@@ -562,7 +561,7 @@ __global__ __launch_bounds__(kBlock) void band_scan_kernel(TilePlan tp, const in
 // workgroup writes its run of every band at the offset the scan gave it: an
 // LDS counter per band hands out the places in the run (so the order inside
 // a run is arbitrary; the tile pass orders what it sums). An entry is the
-// sample index k and its anchor bits.
+// sample index k.
 // Dynamic LDS: 2 * max_bands ints.
 __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TilePlan tp, BandWs w,
                                                                const uint32_t* __restrict__ anchor, int max_bands)
@@ -628,10 +627,10 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 
 // Tile kernel. LPU lanes per lane group (4 channels per lane). The band's
 // anchor bins (anchor rows r0-1..r1-1, columns c0-1..c1-1) are dealt out to
-// the kTileBlock / LPU groups in blocks of kRectRows x kRectCols bins. An
-// entry anchored at (x0, y0) reaches the pixels (x0..x0+1, y0..y0+1), so a
-// group's block of bins reaches (kRectRows + 1) x (kRectCols + 1) pixels:
-// its own kRectRows x kRectCols and a halo row above and column to the left,
+// the kTileBlock / LPU groups in blocks of kRectRows x RW bins. An entry
+// anchored at (x0, y0) reaches the pixels (x0..x0+1, y0..y0+1), so a
+// group's block of bins reaches (kRectRows + 1) x (RW + 1) pixels: its own
+// kRectRows x RW and a halo row above and column to the left,
 // which belong to the neighbouring groups. Every entry's grad_output row is
 // thus loaded once and applied to all four corners; after the walk the
 // groups hand their halos to their neighbours through LDS, which add them in
@@ -640,12 +639,12 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 // (buffer spans stay below 2^31 bytes): such a load returns zeros.
 constexpr uint32_t kNoRowBytes = 1u << 31;
 
-template <typename T, int LPU, bool BUF>
+template <typename T, int LPU, bool BUF, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, const float* __restrict__ loc,
     const float* __restrict__ attn, T* __restrict__ grad_value, float* __restrict__ partial, int accumulate)
 {
-    constexpr int RH = kRectRows, RW = kRectCols;
+    constexpr int RH = kRectRows;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
     // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
@@ -1187,21 +1186,34 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
     return hipGetLastError();
 }
 
+template <typename T, int LPU, int RW>
+static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
+                               const float* loc, const float* attn, void* grad_value, float* partial,
+                               int accumulate, hipStream_t stream)
+{
+    const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
+    const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
+    if (buffer_loads_ok(slab_rows_bytes))
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           stream, g, tp, w, static_cast<const T*>(grad_out), loc, attn,
+                           static_cast<T*>(grad_value), partial, accumulate);
+    else
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
+                           stream, g, tp, w, static_cast<const T*>(grad_out), loc, attn,
+                           static_cast<T*>(grad_value), partial, accumulate);
+}
+
 template <typename T, int LPU>
 static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
                                  const float* loc, const float* attn,
                                  void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
-    const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
-    const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
-    if (buffer_loads_ok(slab_rows_bytes))
-        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g,
-                           tp, w, static_cast<const T*>(grad_out), loc, attn, static_cast<T*>(grad_value), partial,
-                           accumulate);
+    if (tp.rect_cols == kRectColsSparse)
+        launch_tile_kernel<T, LPU, kRectColsSparse>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate,
+                                                    stream);
     else
-        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
-                           g, tp, w, static_cast<const T*>(grad_out), loc, attn, static_cast<T*>(grad_value), partial,
-                           accumulate);
+        launch_tile_kernel<T, LPU, kRectColsDense>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate,
+                                                   stream);
     if (tp.rpieces > 0)
         hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
                            0, stream, g, tp, partial, static_cast<T*>(grad_value), accumulate);
@@ -1223,10 +1235,10 @@ static hipError_t launch_generic_t(const Geometry& g, const void* grad_out, cons
     return hipGetLastError();
 }
 
-// Workspace of the fast path with grad_value: per-sample anchors and records
-// (20 bytes per sample), per-(band, run) counts and offsets, the band lists
-// (4 bytes per reserved entry) and the float32 partial tiles of split bands.
-// Every piece starts 256-byte aligned.
+// Workspace of the fast path with grad_value: per-sample anchors (4 bytes per
+// sample), per-(band, run) counts and offsets, the band lists (4 bytes per
+// reserved entry) and the float32 partial tiles of split bands. Every piece
+// starts 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws,

@@ -90,6 +90,14 @@ def test_backward_named_workload_full_size(num, gpu_device):
     _check_backward(d, gpu_device, f"workload {num} {wl.name}")
 
 
+def test_backward_decoder_workload_full_size(gpu_device):
+    """The decoder workload's shapes (B=8, N_q=300 clustered queries over the
+    L=22223 pyramid) with a grad_output: samples are sparse against the
+    pixels, so the tile pass takes its wide-block plan."""
+    d = make_workload(3, grad_seed=1003)
+    _check_backward(d, gpu_device, "workload 3 decoder, backward")
+
+
 # ------------------------------------------------------------- flag sweep ---
 
 SWEEP = list(itertools.product(["BLNC", "BNLC"], ["BQHLP2", "B2QHLP"], [False, True], ["zeros", "border"]))
@@ -252,6 +260,15 @@ def test_many_runs_in_one_pass(gpu_device):
     79 runs (more than the 64 a single ballot covers)."""
     d = _mk(levels=((200, 200), (10, 12)), B=1, N_h=1, N_q=40000, C_h=8, N_p=4, seed=29, loc_range=(0.0, 1.0))
     _check_backward(d, gpu_device, "many runs in one pass")
+
+
+def test_sparse_samples_wide_blocks_and_split_band(gpu_device):
+    """16,000 samples per (b, h, level) against 18,000 pixels in the large
+    level: the tile pass takes 2x4-bin blocks per lane group (sparse shape),
+    and the one band of the 6x7 level holds every sample of that level, so it
+    is split into chunks whose partial tiles the reduction adds."""
+    d = _mk(levels=((120, 150), (6, 7)), B=1, N_h=2, N_q=4000, C_h=32, N_p=4, seed=31, loc_range=(-0.05, 1.05))
+    _check_backward(d, gpu_device, "sparse shape, split band")
 
 
 def test_autograd_function_matches_oracle(gpu_device):
