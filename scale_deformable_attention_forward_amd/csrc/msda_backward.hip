@@ -382,10 +382,15 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
 #pragma unroll
                     for (int i = 1; i < VEC; ++i) d[k] = __builtin_fmaf(G[i], v[k][i], d[k]);
                 }
-                const float gxw = 1.f - r.fx, gyw = 1.f - r.fy;
-                float pa = gxw * gyw * d[0] + r.fx * gyw * d[1] + gxw * r.fy * d[2] + r.fx * r.fy * d[3];
-                float px = gyw * (d[1] - d[0]) + r.fy * (d[3] - d[2]);
-                float py = gxw * (d[2] - d[0]) + r.fx * (d[3] - d[1]);
+                // interpolate along x first: r0 and r1 are the dots of the
+                // two corner rows' x-interpolations, so <G, S> = r0 + fy (r1 - r0),
+                // <G, dS/dy> = r1 - r0 and <G, dS/dx> = e0 + fy (e1 - e0) with
+                // e0, e1 the rows' x-differences
+                const float e0 = d[1] - d[0], e1 = d[3] - d[2];
+                const float r0 = __builtin_fmaf(r.fx, e0, d[0]), r1 = __builtin_fmaf(r.fx, e1, d[2]);
+                float py = r1 - r0;
+                float pa = __builtin_fmaf(r.fy, py, r0);
+                float px = __builtin_fmaf(r.fy, e1 - e0, e0);
                 pa = group_sum<LPU>(pa);
                 px = group_sum<LPU>(px);
                 py = group_sum<LPU>(py);
