@@ -287,18 +287,18 @@ __device__ __forceinline__ void store_results(const Geometry& g, const float4* s
         const int si = s0 + s;
         const int idx = ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si;
         const float4 res = s_res[gi * row + s];
-        if (grad_attn) grad_attn[idx] = res.x;
+        if (grad_attn) nt_store(grad_attn + idx, res.x);
         if (grad_loc) {
             if (g.b2q) {
                 const int plane = g.Nq * g.Nh * g.S;
                 const int j = ui.b * 2 * plane + (ui.q * g.Nh + ui.h) * g.S + si;
-                grad_loc[j] = res.y;
-                grad_loc[j + plane] = res.z;
+                nt_store(grad_loc + j, res.y);
+                nt_store(grad_loc + j + plane, res.z);
             } else if (g.loc_pair_aligned) {
-                *reinterpret_cast<float2*>(grad_loc + 2 * idx) = make_float2(res.y, res.z);
+                nt_store2(grad_loc + 2 * idx, res.y, res.z);
             } else {
-                grad_loc[2 * idx] = res.y;
-                grad_loc[2 * idx + 1] = res.z;
+                nt_store(grad_loc + 2 * idx, res.y);
+                nt_store(grad_loc + 2 * idx + 1, res.z);
             }
         }
     }
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
-            kk[u] = i < m_cnt ? w.k[lbase + p0 + i] : 0u;
+            kk[u] = i < m_cnt ? __builtin_nontemporal_load(w.k + lbase + p0 + i) : 0u;  // read once
         }
         // each entry's record (anchor corner, fractions, attention weight),
         // recomputed from its location and weight exactly as the backward
@@ -974,7 +974,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         return;
     }
     // one chunk of a split band: its partial tile, pixel-major (band-local
-    // row-major pixel index), C_h floats per pixel
+    // row-major pixel index), C_h floats per pixel (stored non-temporal too:
+    // the reduction reads it back once, and in L2 it would only displace the
+    // rows the other tile jobs re-read)
     float* slot = partial + (size_t)slab * tp.part_per_slab + t.part +
                   (size_t)(band * t.nch + chunk) * (t.R * t.CW) * g.Ch;
 #pragma unroll
@@ -982,7 +984,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int j = 1; j <= RW; ++j) {
             const int py = by0 - 1 + i, px = bx0 - 1 + j;
-            if (py < th && px < tw) *reinterpret_cast<float4*>(slot + (py * tw + px) * g.Ch + ch) = acc[i][j];
+            if (py < th && px < tw)
+                nt_store4(slot + (py * tw + px) * g.Ch + ch, acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w);
         }
 }
 

@@ -180,7 +180,52 @@ __device__ __forceinline__ float load_f32(const uint16_t* p) { return bf16_to_f3
 __device__ __forceinline__ void store_f32(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f32(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
-// Load VEC consecutive elements of storage type T as float32.
+// Non-temporal stores, for final outputs that no kernel of the call reads
+// again: their lines are not kept in L2, which stays with the tensors the
+// gathers re-read (measured: forward 121 -> 113 us, and the backward's
+// kernels faster too, at the encoder shape).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void nt_store(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store(uint16_t* p, uint16_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store2(float* p, float a, float b)
+{
+    f32x2_t t;
+    t.x = a;
+    t.y = b;
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x2_t*>(p));
+}
+__device__ __forceinline__ void nt_store4(float* p, float a, float b, float c, float d)
+{
+    f32x4_t t;
+    t.x = a;
+    t.y = b;
+    t.z = c;
+    t.w = d;
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void nt_store2u(uint32_t* p, uint32_t a, uint32_t b)
+{
+    u32x2_t t;
+    t.x = a;
+    t.y = b;
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void nt_store4u(uint32_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    u32x4_t t;
+    t.x = a;
+    t.y = b;
+    t.z = c;
+    t.w = d;
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
+// Load VEC consecutive elements of storage type T as float32; store VEC
+// float32 values as T (non-temporal: only final outputs are stored this way).
 template <typename T, int VEC> struct VecIO;
 
 template <int VEC> struct VecIO<float, VEC> {
@@ -200,12 +245,12 @@ template <int VEC> struct VecIO<float, VEC> {
     static __device__ __forceinline__ void store(float* p, const float (&v)[VEC])
     {
         if constexpr (VEC == 4) {
-            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+            nt_store4(p, v[0], v[1], v[2], v[3]);
         } else if constexpr (VEC == 2) {
-            *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+            nt_store2(p, v[0], v[1]);
         } else {
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) p[i] = v[i];
+            for (int i = 0; i < VEC; ++i) nt_store(p + i, v[i]);
         }
     }
 };
@@ -241,15 +286,15 @@ template <int VEC> struct VecIO<uint16_t, VEC> {
             for (int i = 0; i < VEC / 2; ++i)
                 w[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
             if constexpr (VEC == 8) {
-                *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+                nt_store4u(reinterpret_cast<uint32_t*>(p), w[0], w[1], w[2], w[3]);
             } else if constexpr (VEC == 4) {
-                *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+                nt_store2u(reinterpret_cast<uint32_t*>(p), w[0], w[1]);
             } else {
-                *reinterpret_cast<uint32_t*>(p) = w[0];
+                nt_store(reinterpret_cast<uint32_t*>(p), w[0]);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) p[i] = f32_to_bf16_rne(v[i]);
+            for (int i = 0; i < VEC; ++i) nt_store(p + i, f32_to_bf16_rne(v[i]));
         }
     }
 };
