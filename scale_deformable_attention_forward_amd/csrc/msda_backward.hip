@@ -178,12 +178,15 @@ __device__ __forceinline__ BwdRecord make_record(const Geometry& g, float ux, fl
     return r;
 }
 
-// Per-sample anchors for the destination-tiled grad_value pass, laid out
+// Per-sample data for the destination-tiled grad_value pass, laid out
 // [b * N_h + h][l][q][p]: the anchor corner packed (x0 + 2) | (y0 + 2) << 16
-// (x0, y0 >= -2 after the clamp above). The tile kernel recomputes the rest
-// of a sample's record from its location and attention weight.
+// (x0, y0 >= -2 after the clamp above) on its own for the bucketing kernels,
+// and (anchor bits, fx, fy, A) as one 16-byte record for the tile kernel,
+// stored non-temporal: it is read about once, by the tile kernel, and would
+// otherwise take cache room from the inputs.
 struct AnchorWs {
     uint32_t* anchor;
+    float4* rec;
 };
 
 // Stage one record per (unit, sample) of the chunk [s0, s0 + sc).
@@ -267,6 +270,7 @@ __device__ __forceinline__ void stage_fast_records(const Geometry& g, const floa
                 const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
                 const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
                 ws.anchor[k] = an;
+                nt_store4(reinterpret_cast<float*>(ws.rec + k), __uint_as_float(an), r.fx, r.fy, a);
             }
         }
         s_rec[gi * row + s] = f;
@@ -413,6 +417,7 @@ struct BandWs {
     int* cnt;            // [slabs][bands][nwg]
     int* off;            // [slabs][bands * nwg + 1], exclusive prefix of cnt per slab
     uint32_t* k;         // list entries: sample indices k
+    const float4* rec;   // AnchorWs::rec
 };
 
 struct LevelTiles {
@@ -646,8 +651,8 @@ constexpr uint32_t kNoRowBytes = 1u << 31;
 
 template <typename T, int LPU, bool BUF, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
-    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, const float* __restrict__ loc,
-    const float* __restrict__ attn, T* __restrict__ grad_value, float* __restrict__ partial, int accumulate)
+    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
+    float* __restrict__ partial, int accumulate)
 {
     constexpr int RH = kRectRows;
     constexpr int E = kTileEntries;
@@ -683,6 +688,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
     const size_t lbase = (size_t)slab * tp.cap;
+    const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
     // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
@@ -740,28 +746,24 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             const int i = tid + u * kTileBlock;
             kk[u] = i < m_cnt ? __builtin_nontemporal_load(w.k + lbase + p0 + i) : 0u;  // read once
         }
-        // each entry's record (anchor corner, fractions, attention weight),
-        // recomputed from its location and weight exactly as the backward
-        // kernel computed it
-        float ux[kStage], uy[kStage];
+        // each entry's record (anchor corner, fractions, attention weight) as
+        // the backward kernel wrote it (read about once)
+        f32x4_t rc[kStage];
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
-            const int q = fdiv((int)kk[u], g.np_div);
-            const int si = l * g.Np + (int)kk[u] - q * g.Np;
-            ux[u] = uy[u] = ra[u] = 0.f;
-            if (tid + u * kTileBlock < m_cnt) {
-                read_loc(g, loc, b, q, h, si, ux[u], uy[u]);
-                ra[u] = attn[((b * g.Nq + q) * g.Nh + h) * g.S + si];
-            }
+            rc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (tid + u * kTileBlock < m_cnt)
+                rc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(srec + kk[u]));
         }
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
             if (i >= m_cnt) continue;
             int x0, y0;
-            const BwdRecord rc = make_record(g, ux[u], uy[u], ra[u], t.H, t.W, t.start, x0, y0);
-            rfx[u] = rc.fx;
-            rfy[u] = rc.fy;
+            unpack_anchor(__float_as_uint(rc[u].x), x0, y0);
+            rfx[u] = rc[u].y;
+            rfy[u] = rc[u].z;
+            ra[u] = rc[u].w;
             bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
             atomicAdd(&s_cursor[bn[u]], 1);
         }
@@ -1083,7 +1085,7 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const T* vslab = value + slab_off;
     float* gslab = gacc ? gacc + slab_off : nullptr;
     const T* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
-    const AnchorWs no_ws = {nullptr};
+    const AnchorWs no_ws = {nullptr, nullptr};
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
@@ -1196,32 +1198,28 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
 
 template <typename T, int LPU, int RW>
 static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
-                               const float* loc, const float* attn, void* grad_value, float* partial,
-                               int accumulate, hipStream_t stream)
+                               void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
     const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
     if (buffer_loads_ok(slab_rows_bytes))
         hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           stream, g, tp, w, static_cast<const T*>(grad_out), loc, attn,
-                           static_cast<T*>(grad_value), partial, accumulate);
+                           stream, g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value),
+                           partial, accumulate);
     else
         hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           stream, g, tp, w, static_cast<const T*>(grad_out), loc, attn,
-                           static_cast<T*>(grad_value), partial, accumulate);
+                           stream, g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value),
+                           partial, accumulate);
 }
 
 template <typename T, int LPU>
 static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
-                                 const float* loc, const float* attn,
                                  void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     if (tp.rect_cols == kRectColsSparse)
-        launch_tile_kernel<T, LPU, kRectColsSparse>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate,
-                                                    stream);
+        launch_tile_kernel<T, LPU, kRectColsSparse>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
     else
-        launch_tile_kernel<T, LPU, kRectColsDense>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate,
-                                                   stream);
+        launch_tile_kernel<T, LPU, kRectColsDense>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
     if (tp.rpieces > 0)
         hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
                            0, stream, g, tp, partial, static_cast<T*>(grad_value), accumulate);
@@ -1243,10 +1241,10 @@ static hipError_t launch_generic_t(const Geometry& g, const void* grad_out, cons
     return hipGetLastError();
 }
 
-// Workspace of the fast path with grad_value: per-sample anchors (4 bytes per
-// sample), per-(band, run) counts and offsets, the band lists (4 bytes per
-// reserved entry) and the float32 partial tiles of split bands. Every piece
-// starts 256-byte aligned.
+// Workspace of the fast path with grad_value: per-sample anchors and records
+// (20 bytes per sample), per-(band, run) counts and offsets, the band lists
+// (4 bytes per reserved entry) and the float32 partial tiles of split bands.
+// Every piece starts 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, AnchorWs* aws, BandWs* bws,
@@ -1265,11 +1263,13 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     };
     AnchorWs a;
     a.anchor = reinterpret_cast<uint32_t*>(take(ns * 4));
+    a.rec = reinterpret_cast<float4*>(take(ns * 16));
     BandWs w;
     const size_t runs = nb * (size_t)tp.nwg;
     w.cnt = reinterpret_cast<int*>(take(slabs * runs * 4));
     w.off = reinterpret_cast<int*>(take(slabs * (runs + 1) * 4));
     w.k = reinterpret_cast<uint32_t*>(take(cap * 4));
+    w.rec = a.rec;
     float* part = reinterpret_cast<float*>(take(slabs * (size_t)tp.part_per_slab * 4));
     if (aws) *aws = a;
     if (bws) *bws = w;
@@ -1294,15 +1294,14 @@ static hipError_t launch_fast_typed(const Geometry& g, int lpu, const void* grad
 
 template <typename T>
 static hipError_t launch_tiles_typed(const Geometry& g, const TilePlan& tp, int lpu, BandWs w, const void* grad_out,
-                                     const float* loc, const float* attn,
                                      void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
     switch (lpu) {
-    case 1: return launch_tiles_t<T, 1>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
-    case 2: return launch_tiles_t<T, 2>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
-    case 4: return launch_tiles_t<T, 4>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
-    case 8: return launch_tiles_t<T, 8>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
-    case 16: return launch_tiles_t<T, 16>(g, tp, w, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    case 1: return launch_tiles_t<T, 1>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 2: return launch_tiles_t<T, 2>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 4: return launch_tiles_t<T, 4>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 8: return launch_tiles_t<T, 8>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    case 16: return launch_tiles_t<T, 16>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1314,7 +1313,7 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                                 void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
                                 hipStream_t stream)
 {
-    AnchorWs ws = {nullptr};
+    AnchorWs ws = {nullptr, nullptr};
     BandWs bw = {};
     float* partial = nullptr;
     if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw, &partial);
@@ -1332,9 +1331,8 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
                        bw, ws.anchor, max_bands);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, loc, attn, grad_value, partial, accumulate,
-                                               stream)
-                : launch_tiles_typed<float>(g, tp, lpu, bw, grad_out, loc, attn, grad_value, partial, accumulate, stream);
+    return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
+                : launch_tiles_typed<float>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream);
 }
 
 template <typename T>

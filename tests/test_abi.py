@@ -145,9 +145,9 @@ def test_workspace_size(lib):
     sz = ctypes.c_size_t(123)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
     samples = 1 * 5 * 2 * 2 * 2
-    # a 4 B anchor per sample, plus band lists of 4 B per entry with at least
-    # 2 entries per sample
-    assert sz.value >= (4 + 2 * 4) * samples and sz.value % 256 == 0
+    # a 4 B anchor and a 16 B record per sample, plus band lists of 4 B per
+    # entry with at least 2 entries per sample
+    assert sz.value >= (20 + 2 * 4) * samples and sz.value % 256 == 0
     # C_h = 6 takes the generic path: no workspace for float32 ...
     prob, keep = _prob(C_h=6)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
@@ -159,12 +159,12 @@ def test_workspace_size(lib):
     # bfloat16 with C_h = 8 covers both paths
     prob, keep = _prob(value_dtype=torch.bfloat16)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
-    assert sz.value >= max((4 + 2 * 4) * samples, 1 * 30 * 2 * 8 * 4)
+    assert sz.value >= max((20 + 2 * 4) * samples, 1 * 30 * 2 * 8 * 4)
 
 
 def test_workspace_size_encoder_shape(lib):
     # 2 x 22223 queries, 8 heads, 4 levels x 4 points, 32 channels: per-sample
-    # anchors (4 B), 2 to 4 list entries of 4 B per sample, plus partial
+    # anchors (4 B), records (16 B), 2 to 4 list entries of 4 B per sample, plus partial
     # tiles of the split coarse levels
     levels = ((100, 167), (50, 84), (25, 42), (13, 21))
     starts = (0, 16700, 20900, 21950)
@@ -172,7 +172,7 @@ def test_workspace_size_encoder_shape(lib):
     sz = ctypes.c_size_t(0)
     assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
     samples = 2 * 22223 * 8 * 16
-    assert (4 + 8) * samples <= sz.value <= (4 + 16) * samples * 1.5
+    assert (20 + 8) * samples <= sz.value <= (20 + 16) * samples * 1.5
 
 
 def test_bf16_backward_needs_workspace(lib):
