@@ -127,13 +127,13 @@ msda_status msda_forward(const msda_problem* problem, const void* value,
  * The backward takes one of two paths per call:
  *  - destination-tiled (C_h % 4 == 0, C_h <= 64, value / grad_output /
  *    grad_value aligned to 4 elements, B * N_h <= 65535): for
- *    S = B*N_q*N_h*N_l*N_p samples, 4 bytes per sample (its anchor
- *    corner), per-(batch, head, pixel band, run of samples) counts and
- *    offsets, band lists of 4-byte sample indices with room for 2 entries
- *    per sample (4 on levels wider than one band), and float32 partial
- *    tiles for the bands of coarse levels that are split over several
- *    workgroups; about 145 MB for 2 x 22223 queries, 8 heads, 4 levels,
- *    4 points, 32 channels;
+ *    S = B*N_q*N_h*N_l*N_p samples, 20 bytes per sample (anchor corner,
+ *    fractions, attention weight), per-(batch, head, pixel band, run of
+ *    samples) counts and offsets, band lists of 4-byte sample indices with
+ *    room for 2 entries per sample (4 on levels wider than one band), and
+ *    float32 partial tiles for the bands of coarse levels that are split over
+ *    several workgroups; about 236 MB for 2 x 22223 queries, 8 heads,
+ *    4 levels, 4 points, 32 channels;
  *  - generic (any other shape or alignment): a float32 array of value's
  *    element count for bfloat16, nothing for float32.
  * The size returned covers both. The contents are scratch and need no
