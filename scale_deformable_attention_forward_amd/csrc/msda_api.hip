@@ -181,9 +181,11 @@ bool fast_backward_shape(const msda_problem& p)
 // per job, and wider blocks halve the jobs), else kRectColsDense (a
 // narrower accumulator window is cheaper per entry). The choice depends on
 // the shapes only. At most kMaxBandsPerLevel bands per level. A
-// band whose list is expected to hold more than two LDS passes of entries
+// band whose list is expected to hold more than three LDS passes of entries
 // (coarse levels, where many samples land on each pixel) is split into
-// chunks of its list, one workgroup each; each chunk writes a float32 partial
+// chunks of its list of about three passes, one workgroup each (smaller
+// chunks add partial tiles and reduction work, larger ones make the tile
+// pass wait on its longest jobs); each chunk writes a float32 partial
 // tile and the reduction pass adds a band's partial tiles in chunk order.
 // Returns false if a level cannot be tiled that way.
 bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
@@ -232,7 +234,7 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         if (rb * cb > msda::kMaxBandsPerLevel) return false;
         // list entries of one band if locations spread evenly
         const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;
-        int64_t chunks = (expect + 2 * msda::kTileEntries - 1) / (2 * msda::kTileEntries);
+        int64_t chunks = (expect + 3 * msda::kTileEntries - 1) / (3 * msda::kTileEntries);
         chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, std::min<int64_t>(nwg, 1024)));  // >= 1 run each
         tp->rows[l] = (int32_t)rows;
         tp->rows_div[l] = msda::make_fastdiv((uint32_t)rows);

@@ -670,7 +670,10 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int tid = threadIdx.x;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int slab = lb / tp.jobs;
-    const int job = lb - slab * tp.jobs;
+    // jobs run in reverse plan order: the coarse levels' jobs (dense bands,
+    // several passes each) start first, so the kernel does not end waiting
+    // on one of them
+    const int job = tp.jobs - 1 - (lb - slab * tp.jobs);
     const int b = slab / g.Nh, h = slab - b * g.Nh;
 
     int l = 0;
