@@ -88,7 +88,7 @@ constexpr int kRectColsDense = 2;        //   2 columns where samples are dense 
 constexpr int kRectColsSparse = 4;       //   4 where they are sparse (twice the band width: half the jobs)
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
-constexpr int kBandBlock = 256;          // threads of the bucketing kernels
+constexpr int kBandBlock = 512;          // threads of the bucketing kernels
 constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
 constexpr int kReduceF4 = 256;           // float4s of a band one reduction workgroup adds up
