@@ -17,7 +17,8 @@
 //     corners, form S, dS/dx and dS/dy, reduce the three dot products with
 //     DPP, and grad_A / grad_loc leave through LDS as coalesced stores. When
 //     grad_value is wanted, the staging also writes each sample's anchor
-//     corner (x0, y0) to the workspace.
+//     corner (x0, y0) and a record of its anchor, fractions and weight to the
+//     workspace.
 //  2. grad_value by destination instead of by source, so no float atomics and
 //     no order-dependent sums (global float atomics run at about one 128-byte
 //     line per request and LDS float atomics are an order of magnitude slower
@@ -193,7 +194,7 @@ struct AnchorWs {
 __device__ __forceinline__ void stage_records(const Geometry& g, const float* __restrict__ loc,
                                               const float* __restrict__ attn, BwdRecord* s_rec, int row,
                                               int u0, int upb, int s0, int sc, const FastDiv& scd,
-                                              const int4* s_lv, AnchorWs ws)
+                                              const int4* s_lv)
 {
     for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
         const int gi = fdiv(i, scd);
@@ -211,11 +212,6 @@ __device__ __forceinline__ void stage_records(const Geometry& g, const float* __
             const float a = attn[((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.S + si];
             int x0, y0;
             r = make_record(g, ux, uy, a, H, W, start, x0, y0);
-            if (ws.anchor) {
-                const int k = (((ui.b * g.Nh + ui.h) * g.Nl + l) * g.Nq + ui.q) * g.Np + (si - l * g.Np);
-                const uint32_t an = (uint32_t)(x0 + 2) | ((uint32_t)(y0 + 2) << 16);
-                ws.anchor[k] = an;
-            }
         }
         s_rec[gi * row + s] = r;
     }
@@ -1088,13 +1084,12 @@ __global__ __launch_bounds__(kBlock) void backward_generic_kernel(Geometry g, in
     const T* vslab = value + slab_off;
     float* gslab = gacc ? gacc + slab_off : nullptr;
     const T* grow = grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch;
-    const AnchorWs no_ws = {nullptr, nullptr};
 
     for (int s0 = 0; s0 < g.S; s0 += sc_max) {
         const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
         const FastDiv& scd = cdiv.of(sc, sc_max);
-        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv, no_ws);
+        stage_records(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv);
         __syncthreads();
         if (unit_ok) {
             for (int s = 0; s < sc; ++s) {
