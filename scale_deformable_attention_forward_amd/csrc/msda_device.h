@@ -180,10 +180,11 @@ __device__ __forceinline__ float load_f32(const uint16_t* p) { return bf16_to_f3
 __device__ __forceinline__ void store_f32(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f32(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
-// Non-temporal stores, for final outputs that no kernel of the call reads
-// again: their lines are not kept in L2, which stays with the tensors the
-// gathers re-read (measured: forward 121 -> 113 us, and the backward's
-// kernels faster too, at the encoder shape).
+// Non-temporal stores, for final outputs and for workspace data that is read
+// back about once: their lines are not kept in L2 (nor in the last-level
+// cache), which stay with the tensors the gathers re-read (measured: forward
+// 121 -> 113 us, and the backward's kernels faster too, at the encoder
+// shape).
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -225,7 +226,8 @@ __device__ __forceinline__ void nt_store4u(uint32_t* p, uint32_t a, uint32_t b, 
 }
 
 // Load VEC consecutive elements of storage type T as float32; store VEC
-// float32 values as T (non-temporal: only final outputs are stored this way).
+// float32 values as T (non-temporal: only final outputs are stored this
+// way).
 template <typename T, int VEC> struct VecIO;
 
 template <int VEC> struct VecIO<float, VEC> {
