@@ -63,8 +63,6 @@ def bind(path):
     lib.oracle_forward.restype = i32
     lib.oracle_backward.argtypes = common + [pd] * 7
     lib.oracle_backward.restype = i32
-    lib.oracle_count_inrange_corners.argtypes = [i64] * 6 + [p64, p64] + [i32] * 4 + [pd]
-    lib.oracle_count_inrange_corners.restype = i64
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
@@ -156,26 +154,3 @@ def backward(grad_output, value, spatial_shapes, level_start_index, sampling_loc
     if rc != 0:
         raise ValueError(f"oracle_backward rejected the problem (code {rc})")
     return gv, gl, ga
-
-
-def count_inrange_corners(spatial_shapes, level_start_index, sampling_locations,
-                          sampling_locations_layout="BQHLP2", align_corners=False,
-                          padding_mode="zeros", coord_fp32=True):
-    """Number of (sample, corner) pairs whose corner lies inside its level."""
-    lib = _load()
-    loc = _f64(sampling_locations)
-    ss, ls = _levels(spatial_shapes, level_start_index)
-    if sampling_locations_layout == "BQHLP2":
-        B, Nq, Nh, Nl, Np, _ = loc.shape
-    else:
-        B, _, Nq, Nh, Nl, Np = loc.shape
-    L = int((ss[:, 0] * ss[:, 1]).sum())
-    i64p = ctypes.POINTER(ctypes.c_int64)
-    n = lib.oracle_count_inrange_corners(B, L, Nq, Nh, Nl, Np, ss.ctypes.data_as(i64p),
-                                         ls.ctypes.data_as(i64p),
-                                         LOC_LAYOUTS[sampling_locations_layout],
-                                         int(bool(align_corners)), PADDINGS[padding_mode],
-                                         int(bool(coord_fp32)), _ptr(loc))
-    if n < 0:
-        raise ValueError("oracle_count_inrange_corners rejected the problem")
-    return int(n)

@@ -263,31 +263,6 @@ int oracle_backward(int64_t B, int64_t L, int64_t Nq, int64_t Nh, int64_t Ch, in
     return 0;
 }
 
-/* Number of (sample, corner) pairs whose corner lies inside its level:
-   the corners the method has to read. */
-int64_t oracle_count_inrange_corners(int64_t B, int64_t L, int64_t Nq, int64_t Nh, int64_t Nl, int64_t Np,
-                                     const int64_t *spatial_shapes, const int64_t *level_start_index,
-                                     int loc_layout, int align_corners, int padding, int coord_fp32,
-                                     const double *loc)
-{
-    prob_t P = {B, L, Nq, Nh, 1, Nl, Np, spatial_shapes, level_start_index,
-                ORACLE_BLNC, loc_layout, align_corners, padding, coord_fp32};
-    if (check(&P)) return -1;
-    int64_t n = 0;
-#pragma omp parallel for collapse(2) reduction(+ : n)
-    for (int64_t b = 0; b < B; ++b)
-        for (int64_t q = 0; q < Nq; ++q)
-            for (int64_t h = 0; h < Nh; ++h)
-                for (int64_t l = 0; l < Nl; ++l)
-                    for (int64_t p = 0; p < Np; ++p) {
-                        corners_t K;
-                        make_corners(&P, l, loc[loc_index(&P, b, q, h, l, p, 0)],
-                                     loc[loc_index(&P, b, q, h, l, p, 1)], &K);
-                        for (int k = 0; k < 4; ++k) n += K.inb[k];
-                    }
-    return n;
-}
-
 /* Threads an OpenMP region of this library uses (for reporting only). */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
 

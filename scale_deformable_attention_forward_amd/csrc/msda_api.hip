@@ -158,12 +158,16 @@ int pick_vec(int64_t C_h, int elem, std::initializer_list<const void*> ptrs)
 int fast_lanes(int64_t C_h) { return 1 << ilog2((int)((C_h + 3) / 4)); }
 
 // The fast backward path needs C_h % 4 == 0, C_h <= 64 (4 channels per lane,
-// at most 16 lanes per pixel), pixel coordinates that pack in 16 bits, and at
-// most 65535 (b, h) slabs (a grid dimension of the bucketing kernels).
+// at most 16 lanes per pixel), pixel coordinates that pack in 16 bits, at
+// most 65535 (b, h) slabs (a grid dimension of the bucketing kernels), and
+// grad_output rows of one batch spanning fewer than 2^31 - 2^20 bytes (the
+// tile pass reads them through a buffer resource with 32-bit byte offsets).
 bool fast_backward_shape(const msda_problem& p)
 {
     if (p.C_h % 4 != 0 || p.C_h > 64) return false;
     if (p.B * p.N_h > 65535) return false;
+    const int64_t elem = p.value_dtype == MSDA_BF16 ? 2 : 4;
+    if (!msda::buffer_loads_ok(p.N_q * p.N_h * p.C_h * elem)) return false;
     for (int64_t l = 0; l < p.N_l; ++l)
         if (p.spatial_shapes[2 * l] > 60000 || p.spatial_shapes[2 * l + 1] > 60000) return false;
     return true;

@@ -219,7 +219,7 @@ __device__ __forceinline__ void stage_records(const Geometry& g, const float* __
 
 // Record of the fast path: fractions, the coordinate slopes times the
 // attention weight, and the four corners' element offsets in value
-// (no_corner<T>() for a corner outside the level).
+// (no_corner<T, BUF>() for a corner outside the level).
 struct BwdFastRecord {
     float fx, fy;
     float akx, aky;  // A * d(pixel)/d(location), 0 where border clamped
@@ -229,13 +229,13 @@ static_assert(sizeof(BwdFastRecord) == 2 * sizeof(float4), "records must tile tw
 
 // Stage one fast-path record per (unit, sample) of the chunk [s0, s0 + sc),
 // and (with ws) the per-sample anchor of the grad_value pass.
-template <typename T>
+template <typename T, bool BUF>
 __device__ __forceinline__ void stage_fast_records(const Geometry& g, const float* __restrict__ loc,
                                                    const float* __restrict__ attn, BwdFastRecord* s_rec, int row,
                                                    int u0, int upb, int s0, int sc, const FastDiv& scd,
                                                    const int4* s_lv, AnchorWs ws)
 {
-    const int32_t nc = no_corner<T>();
+    const int32_t nc = no_corner<T, BUF>();
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     for (int i = threadIdx.x; i < upb * sc; i += blockDim.x) {
         const int gi = fdiv(i, scd);
@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const bool want_dots = grad_loc != nullptr || grad_attn != nullptr;
     const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     const __amdgpu_buffer_rsrc_t vr = value_rsrc(value, BUF ? value_bytes : 0);
-    const int32_t nc = no_corner<T>();
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int u = u0 + grp;
@@ -348,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
         const int sc = min(sc_max, g.S - s0);
         if (s0 > 0) __syncthreads();
         const FastDiv& scd = cdiv.of(sc, sc_max);
-        stage_fast_records<T>(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv, ws);
+        stage_fast_records<T, BUF>(g, loc, attn, s_rec, row, u0, upb, s0, sc, scd, s_lv, ws);
         if (!want_dots) continue;
         __syncthreads();
         if (unit_ok) {
@@ -363,7 +362,8 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
                     } else {
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) v[k][i] = 0.f;
-                        if (lane_ok && ok[k] != nc) VecIO<T, VEC>::load(value + ok[k] + c0, v[k]);
+                        // no_corner<T, false>() is -1
+                        if (lane_ok && ok[k] >= 0) VecIO<T, VEC>::load(value + ok[k] + c0, v[k]);
                     }
                 }
                 if (BUF && !lane_ok) {
@@ -645,7 +645,7 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 // (buffer spans stay below 2^31 bytes): such a load returns zeros.
 constexpr uint32_t kNoRowBytes = 1u << 31;
 
-template <typename T, int LPU, bool BUF, int RW>
+template <typename T, int LPU, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
     float* __restrict__ partial, int accumulate)
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
     // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
-    const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, BUF ? (int64_t)g.Nq * gq * (int64_t)sizeof(T) : 0);
+    const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, (int64_t)g.Nq * gq * (int64_t)sizeof(T));
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
@@ -699,7 +699,6 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     const int gy = grp / gnx, gx = grp - gy * gnx;
     const int by0 = gy * RH, bx0 = gx * RW;  // the group's first bin (bin row 0 is anchor row r0 - 1)
     const bool grp_ok = ch < g.Ch && gy < gny;
-    const T* gl = grow0 + ch;
 
     // acc[a][c] is band-local pixel (by0 - 1 + a, bx0 - 1 + c): rows and
     // columns 1.. are the group's own, row 0 and column 0 its halo
@@ -860,48 +859,25 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
                 b0 = s_bstart[bin];
                 b1 = s_bstart[bin + 1];
             };
-            if constexpr (BUF) {
 #pragma unroll
-                for (int bi = 0; bi < RH; ++bi) {
+            for (int bi = 0; bi < RH; ++bi) {
 #pragma unroll
-                    for (int bj = 0; bj < RW; ++bj) {
-                        int e0, e1;
-                        bin_range(bi, bj, e0, e1);
-                        for (int e = e0; e < e1; e += 4) {
-                            float4 wv[4];
-                            float gv[4][4];
+                for (int bj = 0; bj < RW; ++bj) {
+                    int e0, e1;
+                    bin_range(bi, bj, e0, e1);
+                    for (int e = e0; e < e1; e += 4) {
+                        float4 wv[4];
+                        float gv[4][4];
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                // slots past the bin's end load no row (the buffer
-                                // returns zeros past its end), so whatever
-                                // weights they read add nothing
-                                wv[u] = s_w[e + u];
-                                const uint32_t row = s_row[e + u];
-                                BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
-                            }
-                            add_terms(bi, bj, wv, gv);
+                        for (int u = 0; u < 4; ++u) {
+                            // slots past the bin's end load no row (the buffer
+                            // returns zeros past its end), so whatever
+                            // weights they read add nothing
+                            wv[u] = s_w[e + u];
+                            const uint32_t row = s_row[e + u];
+                            BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
                         }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int bi = 0; bi < RH; ++bi) {
-#pragma unroll
-                    for (int bj = 0; bj < RW; ++bj) {
-                        int e0, e1;
-                        bin_range(bi, bj, e0, e1);
-                        for (int e = e0; e < e1; e += 4) {
-                            float4 wv[4];
-                            float gv[4][4];
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                // slots past the bin's end read a zero-weight slot
-                                const int ei = e + u < e1 ? e + u : m_cnt;
-                                wv[u] = s_w[ei];
-                                VecIO<T, 4>::load(gl + s_row[ei], gv[u]);
-                            }
-                            add_terms(bi, bj, wv, gv);
-                        }
+                        add_terms(bi, bj, wv, gv);
                     }
                 }
             }
@@ -1198,16 +1174,12 @@ template <typename T, int LPU, int RW>
 static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
                                void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
+    // the host sends this path only problems whose grad_output rows of one
+    // batch span fewer than 2^31 - 2^20 bytes (tile_rows_fit), so the walk's
+    // buffer loads reach every row
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
-    const int64_t slab_rows_bytes = (int64_t)g.Nq * g.Nh * g.Ch * (int64_t)sizeof(T);
-    if (buffer_loads_ok(slab_rows_bytes))
-        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, true, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           stream, g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value),
-                           partial, accumulate);
-    else
-        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, false, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0,
-                           stream, g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value),
-                           partial, accumulate);
+    hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g,
+                       tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
 }
 
 template <typename T, int LPU>

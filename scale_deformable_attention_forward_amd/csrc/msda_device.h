@@ -315,12 +315,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t value_rsrc(const void* base, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
-// Element offset that marks "no corner": times the element size it is 2^31,
-// past every byte offset a buffer load may legitimately use.
-template <typename T>
+// Element offset that marks "no corner". With buffer loads it is 2^31 bytes
+// past the base, beyond every byte offset a buffer load may legitimately use,
+// so the load returns zeros. On the plain-pointer path (value tensors of
+// 2^31 - 2^20 bytes or more, where 2^31 / sizeof(T) is a valid element) it is
+// -1, below every valid offset; that path tests for it and skips the load.
+template <typename T, bool BUF>
 __host__ __device__ constexpr int32_t no_corner()
 {
-    return (int32_t)((1u << 31) / sizeof(T));
+    return BUF ? (int32_t)((1u << 31) / sizeof(T)) : -1;
 }
 
 // Whether a value tensor of `bytes` bytes takes the buffer-load path.
@@ -378,8 +381,8 @@ template <int VEC> struct BufIO<uint16_t, VEC> {
 // Gather record of one sample: the four corner weights (x0,y0), (x0+1,y0),
 // (x0,y0+1), (x0+1,y0+1) premultiplied by the attention weight (0 for a
 // corner outside the level), and the element offsets in value of those
-// corners' first channel of the sample's (b, h); no_corner<T>() where the
-// weight is 0.
+// corners' first channel of the sample's (b, h); no_corner<T, BUF>() where
+// the weight is 0.
 struct FwdRecord {
     float4 w;
     int4 o;
@@ -388,7 +391,7 @@ struct FwdRecord {
 // Coordinate map, padding and bilinear corners of one sample at normalised
 // (ux, uy) of level (H, W, start) with attention weight a, for the (b, h)
 // slab starting at element slab_off of value.
-template <typename T>
+template <typename T, bool BUF>
 __device__ __forceinline__ void sampler_record(const Geometry& g, float ux, float uy, float a, int H, int W,
                                                int start, int slab_off, FwdRecord& rec)
 {
@@ -419,7 +422,7 @@ __device__ __forceinline__ void sampler_record(const Geometry& g, float ux, floa
     const uint32_t pstride = (uint32_t)(g.bnlc ? g.Ch : g.Nh * g.Ch);
     const uint32_t o00 = (uint32_t)slab_off + (uint32_t)(start + y0 * W + x0) * pstride;
     const uint32_t orow = (uint32_t)W * pstride;
-    const int32_t nc = no_corner<T>();
+    const int32_t nc = no_corner<T, BUF>();
     rec.w = w;
     rec.o.x = w.x != 0.f ? (int32_t)o00 : nc;
     rec.o.y = w.y != 0.f ? (int32_t)(o00 + pstride) : nc;

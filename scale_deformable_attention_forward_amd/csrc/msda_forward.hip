@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
             const int s = i - gi * sc;
             const int uu = u0 + gi;
             FwdRecord rec = {make_float4(0.f, 0.f, 0.f, 0.f),
-                             make_int4(no_corner<T>(), no_corner<T>(), no_corner<T>(), no_corner<T>())};
+                             make_int4(no_corner<T, BUF>(), no_corner<T, BUF>(), no_corner<T, BUF>(),
+                                       no_corner<T, BUF>())};
             if (uu < g.units) {
                 const int t = fdiv(uu, g.ch_div);
                 const int t2 = fdiv(t, g.nq_div);
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void forward_kernel(Geometry g, int sc_max,
                     uy = loc[2 * idx + 1];
                 }
                 const int slab_off = g.bnlc ? (bb * g.Nh + hh) * g.L * g.Ch : bb * g.L * g.Nh * g.Ch + hh * g.Ch;
-                sampler_record<T>(g, ux, uy, attn[idx], H, W, start, slab_off, rec);
+                sampler_record<T, BUF>(g, ux, uy, attn[idx], H, W, start, slab_off, rec);
             }
             s_rec[gi * row + s] = rec;
         }

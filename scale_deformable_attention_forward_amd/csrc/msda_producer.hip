@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kBlock) void fused_forward_kernel(Geometry g, Produ
         if (loc || attn) store_sample(pg, m0 + r, h, j, ux, uy, A, loc, attn);
         int H, W, start;
         level_of(g.lv, l, H, W, start);
-        sampler_record<T>(g, ux, uy, A, H, W, start, slab_off, s_rec[r * row + j]);
+        sampler_record<T, BUF>(g, ux, uy, A, H, W, start, slab_off, s_rec[r * row + j]);
     });
     __syncthreads();
 

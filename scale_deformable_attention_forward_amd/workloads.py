@@ -159,6 +159,29 @@ def make_inputs(B, levels, N_q, N_h, C_h, N_p, seed, loc_dist="uniform", loc_ran
     return out
 
 
+def make_large_value(B, L, N_h, C_h, seed, value_dtype="fp32", chunk=1 << 25):
+    """value ~ N(0, 1) of shape (B, L, N_h, C_h) for tensors of gigabytes:
+    drawn from ``default_rng(seed)`` directly in float32, ``chunk`` elements
+    at a time (the named workloads draw float64 first; that would need eight
+    bytes per element of host memory here). Returns (value float32,
+    bfloat16 bit patterns or None); with value_dtype "bf16" the float32
+    array holds the exact values of the round-to-nearest-even bfloat16
+    numbers."""
+    rng = np.random.default_rng(seed)
+    n = B * L * N_h * C_h
+    value = np.empty(n, dtype=np.float32)
+    bits = np.empty(n, dtype=np.uint16) if value_dtype == "bf16" else None
+    for i in range(0, n, chunk):
+        part = rng.standard_normal(min(chunk, n - i), dtype=np.float32)
+        if bits is not None:
+            b = bf16_round_bits(part)
+            bits[i:i + len(part)] = b
+            part = bf16_bits_to_f32(b)
+        value[i:i + len(part)] = part
+    shape = (B, L, N_h, C_h)
+    return value.reshape(shape), (None if bits is None else bits.reshape(shape))
+
+
 def make_workload(wl: Workload | int, grad_seed=None):
     """Inputs for a named workload (or its number), plus its mode flags."""
     if isinstance(wl, int):

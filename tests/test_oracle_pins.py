@@ -387,20 +387,6 @@ def test_fp32_coordinate_map_close_to_fp64():
         assert np.abs(a - b).max() > 1e-7
 
 
-def test_inrange_corner_count_matches_numpy():
-    d = _tiny(seed=22, loc_range=(-0.2, 1.2))
-    loc = d["sampling_locations"].astype(np.float32)
-    n = oracle.count_inrange_corners(d["spatial_shapes"], d["level_start_index"], loc)
-    want = 0
-    for l, (H, W) in enumerate(d["spatial_shapes"]):
-        x = (loc[:, :, :, l, :, 0].astype(np.float64) * W - 0.5).astype(np.float32).astype(np.float64)
-        y = (loc[:, :, :, l, :, 1].astype(np.float64) * H - 0.5).astype(np.float32).astype(np.float64)
-        x0, y0 = np.floor(x), np.floor(y)
-        for dx, dy in itertools.product([0, 1], [0, 1]):
-            want += int((((x0 + dx) >= 0) & ((x0 + dx) < W) & ((y0 + dy) >= 0) & ((y0 + dy) < H)).sum())
-    assert n == want
-
-
 def test_oracle_rejects_inconsistent_level_table():
     d = _tiny(seed=23)
     with pytest.raises(ValueError):
