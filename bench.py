@@ -7,10 +7,14 @@ float32, BLNC / BQHLP2, zeros padding, align_corners off; locations
 U[-0.05, 1.05], softmax attention weights, grad_output ~ N(0, 1). Inputs are
 seeded, synthetic, and resident in HBM before the timed region starts.
 
-Prints ONE JSON line. `value` is queries/s of whole steps; `roofline` is the
-dominant launch's algorithmic bytes over its average duration (HIP events on
-the stream the kernels run on) against the 8 TB/s HBM peak; `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same workload on this host.
+Prints ONE JSON line. `value` is queries/s of whole steps. `roofline` prices
+the dominant launch (the backward call) against the ceiling of the memory
+level that serves its gathers: the L2 -> CU path (8 XCDs x 16 L2 channels x
+128 B per clock x 2.4 GHz), measured beside it with the probe library's
+L2-resident read probes; HBM traffic from calibration-free rocprofv3 counters
+(committed summary) is reported beside it against the 8 TB/s HBM peak.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload on this host's cores (and on one core).
 
 `--report` instead times every named workload (forward, and backward where it
 has a grad_output) warm and with cold caches, next to the CPU oracle on all
@@ -33,6 +37,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense float32 matrix-core peak, TFLOP/s
+# L2 -> CU read ceiling: 8 XCDs, each with a 16-channel L2 that returns one
+# 128-byte line per channel per clock, at the 2.4 GHz peak engine clock
+# (the same figure as 256 CUs x 64 B per clock of vector-memory return).
+XCDS, L2_CHANNELS_PER_XCD, L2_BYTES_PER_CLOCK, CLOCK_GHZ = 8, 16, 128, 2.4
+L2_PEAK_GBS = XCDS * L2_CHANNELS_PER_XCD * L2_BYTES_PER_CLOCK * CLOCK_GHZ   # 39,321.6 GB/s
+PROBE_LIB = os.path.join(ROOT, "scale_deformable_attention_forward_amd", "libmsda_probe.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fp32_fwd_bwd_hbm_traffic.txt")
 METRIC = "queries/s and effective gathered HBM GB/s (% of peak), fwd+bwd, 1 MI355X"
 WORKLOAD_NUM = 5                # encoder shapes with grad_output (the forward uses the same arrays)
@@ -47,8 +57,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps with a 1 GiB scratch write before each launch (caches cold)")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the timed steps (no cold-cache timings, probes or CPU oracle): for profiler runs")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_NUM,
+                    help="named workload whose forward+backward a step runs (default: the encoder shape); "
+                         "workloads without a grad_output get one drawn with seed 1000 + workload number")
+    ap.add_argument("--mode-variants", action="store_true",
+                    help="time forward and backward at the square bf16 workload's shapes with one of its "
+                         "modes (padding, location range, dtype, layouts, align_corners) changed at a time")
+    ap.add_argument("--generic-backward", action="store_true",
+                    help="only time the backward's generic path (float atomics into grad_value) at the "
+                         "encoder shape: grad_value is a view one element off 16-byte alignment")
     ap.add_argument("--report", action="store_true",
                     help="time every named workload (GPU warm/cold, CPU oracle all cores / 1 core)")
     ap.add_argument("--producer", action="store_true",
@@ -127,11 +146,13 @@ def byte_counts(d):
 
 
 def measured_traffic():
-    """HBM bytes per forward launch and per backward call, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary scaled by its copy calibration
-    (per-dispatch bytes times dispatches per call), plus the L2 hit rate of each
-    kernel; (None, None, {}) when a kernel source changed since the counters
-    were taken."""
+    """Memory-side bytes per forward launch and per backward call from the
+    committed rocprofv3 counter summary: reads = 32 x TCC_EA0_RDREQ_DRAM_32B
+    (the L2's read requests to memory in 32-byte units, whatever their
+    size), writes = WRITE_SIZE (TCC_EA0_WRREQ in 32- and 64-byte units);
+    both checked there against a plain 1 GiB device copy. Also each kernel's
+    L2 hit rate and atomic request counts. (None, None, {}) when a kernel
+    source changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -140,18 +161,70 @@ def measured_traffic():
         path = os.path.join(ROOT, rel)
         if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
             return None, None, {}
-    ff = rec["copy_calibration"]["fetch_factor"]
-    wf = rec["copy_calibration"]["write_factor"]
     fwd = bwd = 0.0
     per = {}
     for name, c in rec["per_dispatch"].items():
-        b = (c["FETCH_SIZE_KiB"] * ff + c["WRITE_SIZE_KiB"] * wf) * 1024.0 * c["dispatches_per_call"]
-        per[name] = {"hbm_bytes_per_call": b, "l2_hit_pct": c.get("L2_hit_pct")}
+        n = c["dispatches_per_call"]
+        b = (c["read_bytes"] + c["write_bytes"]) * n
+        per[name] = {"hbm_bytes_per_call": b, "read_bytes_per_call": c["read_bytes"] * n,
+                     "write_bytes_per_call": c["write_bytes"] * n, "l2_hit_pct": c.get("L2_hit_pct"),
+                     "tcc_atomic_per_call": c.get("TCC_ATOMIC", 0.0) * n}
         if name.startswith("forward_kernel"):
             fwd += b
-        else:
+        elif c.get("path", "tiled") == "tiled":
             bwd += b
     return fwd, bwd, per
+
+
+def compulsory_bytes(d):
+    """Bytes every launch must move to or from memory at least once: its
+    inputs read and outputs written (value read once however often it is
+    gathered)."""
+    B, N_q, N_h, N_l, N_p = d["attention_weights"].shape
+    C_h = d["value"].shape[-1]
+    s_v = 2 if d["value_dtype"] == "bf16" else 4
+    samples = B * N_q * N_h * N_l * N_p
+    value_b = d["value"].size * s_v
+    out_b = B * N_q * N_h * C_h * s_v
+    loc_b, attn_b = samples * 8, samples * 4
+    return {"forward": value_b + loc_b + attn_b + out_b,
+            # grad_output, value, loc, attn in; grad_value, grad_loc, grad_attn out
+            "backward": out_b + value_b + loc_b + attn_b + value_b + loc_b + attn_b}
+
+
+def probe_ceilings(dev, stream):
+    """Read rates (GB/s) the probe library reaches on this GPU: the vector L1,
+    an L2-resident stream, L2-resident 128-byte rows at random (the gathers'
+    access shape) and an HBM stream; median of 5 timed launches each."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError(f"{PROBE_LIB} is not built: run `python -m scale_deformable_attention_forward_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.msda_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.msda_probe_read.restype = ctypes.c_int
+    lib.msda_probe_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.msda_probe_bytes.restype = ctypes.c_int64
+    blocks = 2048
+    buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cases = (("vector_l1", 0, 16 << 10, 4000), ("l2_stream", 1, 2 << 20, 1000),
+             ("l2_gather_128B_rows", 2, 2 << 20, 1000), ("hbm_stream", 3, 1 << 30, 150))
+    res = {}
+    for name, mode, span, iters in cases:
+        nbytes = lib.msda_probe_bytes(mode, blocks, iters)
+
+        def launch():
+            rc = lib.msda_probe_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, span, mode, blocks, iters,
+                                     ctypes.c_void_p(sink.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"probe {name}: msda_probe_read returned {rc}")
+        ms = time_launches(launch, stream, 5, 2)
+        res[name] = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+    del buf, sink
+    return res
 
 
 # ------------------------------------------------------------------ timing ---
@@ -176,7 +249,7 @@ def time_launches(fn, stream, iters, warmup, cold_buf=None):
 
 
 def stats(ms):
-    return {"ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)),
+    return {"ms_mean": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_max": float(np.max(ms)),
             "ms_p10": float(np.percentile(ms, 10)), "ms_p90": float(np.percentile(ms, 90))}
 
 
@@ -270,24 +343,36 @@ def oracle_rate(d, passes, target_s, threads=None):
 
 
 def cpu_baseline(d, target_s):
-    """The CPU oracle on the same inputs: whole forward+backward steps,
-    repeated until about target_s seconds have run."""
+    """The CPU oracle on the same inputs: whole forward+backward steps on every
+    core this process may run on (os.sched_getaffinity), repeated until about
+    target_s seconds have run; then forward+backward on one core over
+    first-query slices of the workload for about a third of that."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
+    prev = oracle.max_threads()
     args = (d["spatial_shapes"], d["level_start_index"])
     B, N_q = d["attention_weights"].shape[:2]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(d["value"], *args, d["sampling_locations"], d["attention_weights"])
-        oracle.backward(d["grad_output"], d["value"], *args, d["sampling_locations"],
-                        d["attention_weights"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 50:
-            break
-    return {"value": reps * B * N_q / el, "unit": "queries/s", "cores": oracle.max_threads(),
+    oracle.set_threads(cores)
+    try:
+        used = oracle.max_threads()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(d["value"], *args, d["sampling_locations"], d["attention_weights"])
+            oracle.backward(d["grad_output"], d["value"], *args, d["sampling_locations"],
+                            d["attention_weights"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or reps >= 50:
+                break
+    finally:
+        oracle.set_threads(prev)
+    q1, c1, s1 = oracle_rate(d, ("forward", "backward"), target_s / 3, threads=1)
+    return {"value": reps * B * N_q / el, "unit": "queries/s", "cores": used,
             "kind": "oracle",
             "sample": f"{reps} full forward+backward step(s) of the same workload ({reps * B * N_q} "
-                      f"queries, {el:.1f} s), fp64 C oracle with OpenMP"}
+                      f"queries, {el:.1f} s), fp64 C oracle with OpenMP on the {cores} cores of this "
+                      "process's CPU affinity mask",
+            "one_core": {"value": q1, "unit": "queries/s", "cores": c1, "sample": s1}}
 
 
 # ---------------------------------------------------------------- report ---
@@ -328,7 +413,7 @@ def report(a):
         if not a.no_cpu_baseline:
             for name in ("forward", "backward"):
                 tgt = a.cpu_seconds / 4
-                qa, ca, sa = oracle_rate(d, (name,), tgt)
+                qa, ca, sa = oracle_rate(d, (name,), tgt, threads=len(os.sched_getaffinity(0)))
                 q1, c1, s1 = oracle_rate(d, (name,), tgt, threads=1)
                 line[name]["cpu_oracle"] = {"all_cores": {"queries_per_s": qa, "cores": ca, "sample": sa},
                                             "one_core": {"queries_per_s": q1, "cores": c1, "sample": s1}}
@@ -405,11 +490,11 @@ def producer_report(a):
                         ("sampler", None)):
             r = stats(ms[k])
             if flop:
-                tf = flop / (r["ms_mean"] * 1e-3) / 1e12
+                tf = flop / (r["ms_median"] * 1e-3) / 1e12
                 r.update(tflops=tf, frac_of_peak=tf / MFMA_F32_PEAK_TFLOPS)
-            r["queries_per_s"] = M / (r["ms_mean"] * 1e-3)
+            r["queries_per_s"] = M / (r["ms_median"] * 1e-3)
             line[k] = r
-        line["fused_forward"]["two_call_chain_ms"] = line["forward"]["ms_mean"] + line["sampler"]["ms_mean"]
+        line["fused_forward"]["two_call_chain_ms"] = line["forward"]["ms_median"] + line["sampler"]["ms_median"]
         if not a.no_cpu_baseline:
             rows = 2048
             f64 = {k: p[k][:, :rows // w["B"]] for k in ("query", "reference_points")}
@@ -429,6 +514,66 @@ def producer_report(a):
                                   "sample": f"{reps} forward+backward passes over {rows} rows "
                                             f"({el:.1f} s), float64 numpy (BLAS threads)"}
         print(json.dumps(line), flush=True)
+
+
+# -------------------------------------------------------- mode variants ---
+
+def mode_variants(a):
+    """Forward and backward at workload 4's shapes (B=4, the square pyramid,
+    N_q = L) with one mode changed at a time; one JSON line per case."""
+    import torch
+    from scale_deformable_attention_forward_amd import binding
+    from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_inputs
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    wl = WORKLOADS[4]
+    cases = (("as workload 4", "bf16", "BNLC", "B2QHLP", True, "border", (-0.05, 1.05)),
+             ("zeros padding", "bf16", "BNLC", "B2QHLP", True, "zeros", (-0.05, 1.05)),
+             ("border, locations U[0,1]", "bf16", "BNLC", "B2QHLP", True, "border", (0.0, 1.0)),
+             ("fp32 value", "fp32", "BNLC", "B2QHLP", True, "border", (-0.05, 1.05)),
+             ("BLNC/BQHLP2", "bf16", "BLNC", "BQHLP2", True, "border", (-0.05, 1.05)),
+             ("align off", "bf16", "BNLC", "B2QHLP", False, "border", (-0.05, 1.05)),
+             ("fp32 BLNC zeros align-off (workload 2 modes)", "fp32", "BLNC", "BQHLP2", False, "zeros",
+              (-0.05, 1.05)))
+    for name, dtype, vl, ll, align, pad, rng in cases:
+        d = make_inputs(wl.B, wl.levels, wl.num_queries, wl.N_h, wl.C_h, wl.N_p, wl.seed, loc_range=rng,
+                        value_dtype=dtype, value_layout=vl, sampling_locations_layout=ll, grad_seed=1004)
+        d.update(align_corners=align, padding_mode=pad)
+        t = _device_inputs(d, dev)
+        fwd, bwd = _launchers(d, t, stream)
+        fm = time_launches(fwd, stream, a.steps, a.warmup)
+        bm = time_launches(bwd, stream, a.steps, a.warmup)
+        q = wl.B * wl.num_queries
+        print(json.dumps({"case": name, "fwd_ms": float(np.median(fm)), "bwd_ms": float(np.median(bm)),
+                          "queries": q, "bwd_ns_per_query": float(np.median(bm)) * 1e6 / q}), flush=True)
+
+
+# ----------------------------------------------------- generic backward ---
+
+def generic_backward(a, d, t, stream):
+    """Time msda_backward on its generic path (one channel per lane, float
+    atomics into grad_value) at the same shape: a grad_value view 4 bytes off
+    16-byte alignment rules out the tiled path. Prints one JSON line."""
+    import torch
+    from scale_deformable_attention_forward_amd import binding
+    ss, ls = d["spatial_shapes"], d["level_start_index"]
+    n = t["value"].numel()
+    store = torch.empty(n + 1, dtype=t["value"].dtype, device=t["value"].device)
+    gv = store[1:].view(t["value"].shape)
+    gl, ga = torch.empty_like(t["loc"]), torch.empty_like(t["attn"])
+
+    def bwd():
+        binding.msda_backward(t["gout"], t["value"], ss, ls, t["loc"], t["attn"], grad_value=gv,
+                              grad_sampling_locations=gl, grad_attention_weights=ga, stream=stream)
+    ms = time_launches(bwd, stream, a.steps, a.warmup)
+    bc = byte_counts(d)
+    r = stats(ms)
+    r.update({"path": "generic (float atomics)", "queries_per_s": bc["queries"] / (float(np.mean(ms)) * 1e-3),
+              "gbs_counted": bc["backward"]["counted"] / (float(np.mean(ms)) * 1e-3) / 1e9,
+              "global_atomic_lane_ops": 4 * bc["samples"] * d["value"].shape[-1],
+              "counted_corner_updates": bc["counted_corners"]})
+    print(json.dumps(r), flush=True)
 
 
 # ------------------------------------------------------------------ main ---
@@ -457,16 +602,24 @@ def main():
     if a.producer:
         producer_report(a)
         return
+    if a.mode_variants:
+        mode_variants(a)
+        return
     from scale_deformable_attention_forward_amd import binding
     from scale_deformable_attention_forward_amd.workloads import WORKLOADS, make_workload
 
     binding.load_library()   # raises if the HIP library is not built: no fallback
-    wl = WORKLOADS[WORKLOAD_NUM]
-    d = make_workload(WORKLOAD_NUM)
+    wl = WORKLOADS[a.workload]
+    d = make_workload(a.workload)
+    if "grad_output" not in d:
+        d["grad_output"] = make_workload(a.workload, grad_seed=1000 + a.workload)["grad_output"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     t = _device_inputs(d, dev)
     fwd, bwd = _launchers(d, t, stream)
+    if a.generic_backward:
+        generic_backward(a, d, t, stream)
+        return
 
     for _ in range(a.warmup):
         fwd()
@@ -490,45 +643,64 @@ def main():
     span_ms = ev[0][0].elapsed_time(ev[K - 1][2])
     ms_per_step = span_ms / K
 
-    cold = None
-    if a.cold:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    cold, ceil = None, None
+    if not a.quick:
+        # cold caches: a 1 GiB scratch write before every launch (outside the events)
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cold = {"forward": stats(time_launches(fwd, stream, min(K, 30), 2, cold_buf=scratch)),
-                "backward": stats(time_launches(bwd, stream, min(K, 30), 2, cold_buf=scratch))}
+                "backward": stats(time_launches(bwd, stream, min(K, 30), 2, cold_buf=scratch)),
+                "note": "30 launches each, a 1 GiB scratch write before every launch evicts L2 and the "
+                        "256 MB last-level cache"}
         del scratch
+        ceil = probe_ceilings(dev, stream)
 
     bc = byte_counts(d)
+    comp = compulsory_bytes(d)
     Q = bc["queries"]
+    t_fwd, t_bwd, per_kernel = measured_traffic() if a.workload == WORKLOAD_NUM else (None, None, {})
+    traffic = {"forward": t_fwd, "backward": t_bwd}
 
     def kernel_line(name, ms):
         avg_s = float(np.mean(ms)) * 1e-3
-        nominal = bc[name]["nominal"]
-        counted = bc[name]["counted"]
+        nominal, counted = bc[name]["nominal"], bc[name]["counted"]
         r = stats(ms)
         r.update({
             "queries_per_s": Q / avg_s,
             "bytes_nominal": nominal, "bytes_counted": counted,
             "gbs_nominal": nominal / avg_s / 1e9, "gbs_counted": counted / avg_s / 1e9,
-            "frac_counted": counted / avg_s / 1e9 / HBM_PEAK_GBS,
+            "l2_frac_counted": counted / avg_s / 1e9 / L2_PEAK_GBS,
+            "effective_gbs_vs_hbm_peak": counted / avg_s / 1e9 / HBM_PEAK_GBS,
+            "compulsory_bytes": comp[name],
         })
+        tr = traffic[name]
+        r["hbm_traffic_bytes"] = tr
+        if tr is not None:
+            r.update({"hbm_gbs": tr / avg_s / 1e9, "hbm_frac": tr / avg_s / 1e9 / HBM_PEAK_GBS,
+                      "traffic_over_compulsory": tr / comp[name]})
         return r
 
     kf, kb = kernel_line("forward", f_ms), kernel_line("backward", b_ms)
-    t_fwd, t_bwd, per_kernel = measured_traffic()
-    kf["traffic"], kb["traffic"] = t_fwd, t_bwd
     kf["launch"] = "forward_kernel (1 launch)"
     kb["launch"] = "msda_backward call: " + ", ".join(BACKWARD_KERNELS)
     dom_name, dom = ("backward", kb) if kb["ms_mean"] >= kf["ms_mean"] else ("forward", kf)
-    achieved = dom["bytes_nominal"] / (dom["ms_mean"] * 1e-3) / 1e9
     roofline = {
-        "bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": achieved / HBM_PEAK_GBS, "traffic": dom["traffic"],
-        "bytes_per_launch": dom["bytes_nominal"],
-        "launch": dom["launch"],
-        "note": "achieved = algorithmic bytes (nominal per-query figure x queries, 4 corners per sample) "
-                "/ mean HIP-event time of one launch; achieved_counted uses the corners the method must "
-                "read; traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles/)",
-        "achieved_counted": dom["gbs_counted"],
+        "bound": "l2", "kernel": dom_name, "launch": dom["launch"],
+        "achieved": dom["gbs_counted"], "peak": L2_PEAK_GBS, "unit": "GB/s",
+        "frac": dom["gbs_counted"] / L2_PEAK_GBS, "traffic": dom["hbm_traffic_bytes"],
+        "bytes_per_launch": dom["bytes_counted"],
+        "peak_derivation": f"{XCDS} XCDs x {L2_CHANNELS_PER_XCD} L2 channels x {L2_BYTES_PER_CLOCK} B/clock x "
+                           f"{CLOCK_GHZ} GHz (L2 -> CU read path; the gathers hit L2 81-92% of the time)",
+        "probe_measured_gbs": ceil,
+        "frac_of_probe_l2_gather": None if ceil is None else dom["gbs_counted"] / ceil["l2_gather_128B_rows"],
+        "forward_frac": kf["l2_frac_counted"],
+        "hbm": {"traffic_bytes": dom["hbm_traffic_bytes"], "peak": HBM_PEAK_GBS,
+                "achieved": dom.get("hbm_gbs"), "frac": dom.get("hbm_frac"),
+                "compulsory_bytes": dom["compulsory_bytes"],
+                "traffic_over_compulsory": dom.get("traffic_over_compulsory")},
+        "note": "achieved = counted algorithmic bytes of one launch (corners in range with nonzero weight x "
+                "C_h x 4 B, re-gather and scatter counted once each, plus every stream once) / its mean "
+                "HIP-event time on the launch stream; traffic = memory-side bytes per launch from rocprofv3 "
+                "TCC_EA0_RDREQ_DRAM_32B and WRITE_SIZE (profiles/), null once a kernel source changed",
     }
     res = {
         "metric": METRIC,
@@ -541,21 +713,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if wl.value_dtype == "bf16" else "f32",
         "data": "synthetic (seeded Deformable-DETR-shaped pyramid, no dataset)",
         "config": {"workload": f"{wl.name} forward+backward: B={wl.B}, levels={list(wl.levels)}, "
-                               f"L=N_q={wl.L}, N_h={wl.N_h}, C_h={wl.C_h}, N_l={wl.N_l}, N_p={wl.N_p}, "
-                               "BLNC/BQHLP2, zeros padding, align_corners=False",
+                               f"L={wl.L}, N_q={wl.num_queries}, N_h={wl.N_h}, C_h={wl.C_h}, N_l={wl.N_l}, "
+                               f"N_p={wl.N_p}, {wl.value_dtype}, {wl.value_layout}/{wl.sampling_locations_layout}, "
+                               f"{wl.padding_mode} padding, align_corners={wl.align_corners}",
                    "global_batch": wl.B, "queries_per_step": Q, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {"forward": kf, "backward": kb},
+        "cold_caches": cold,
         "per_kernel_counters": per_kernel,
         "counted_corner_fraction": bc["counted_fraction"],
         "wall_s_timed": wall,
     }
-    if cold is not None:
-        res["cold_caches"] = cold
-    if not a.no_cpu_baseline:
+    if not (a.no_cpu_baseline or a.quick):
         res["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 

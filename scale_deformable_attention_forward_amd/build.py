@@ -1,4 +1,5 @@
-"""Build libmsda.so (the gfx950 HIP library behind include/msda.h) in-tree.
+"""Build libmsda.so (the gfx950 HIP library behind include/msda.h) and the
+benchmark's probe library libmsda_probe.so in-tree.
 
 Usage: python -m scale_deformable_attention_forward_amd.build
 """
@@ -16,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsda.so")
 SOURCES = ["msda_api.hip", "msda_forward.hip", "msda_backward.hip", "msda_producer.hip"]
+PROBE_LIB = os.path.join(PKG, "libmsda_probe.so")
+PROBE_SOURCES = ["msda_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -27,12 +30,12 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-munsafe-fp-atomics", f"-I{INCLUDE}"]
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source in parallel, link libmsda.so, replace it atomically."""
+def _build(sources, lib_path, verbose):
+    """Compile `sources` in parallel, link them into `lib_path`, replace it atomically."""
     with tempfile.TemporaryDirectory(prefix="msda_build_") as tmp:
         procs = []
         objs = []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -52,15 +55,22 @@ def build_library(verbose: bool = False) -> str:
         if failed:
             msg = "\n\n".join(" ".join(c) + "\n" + t for c, t in failed)
             raise RuntimeError(f"hipcc failed:\n{msg}")
-        tmp_lib = os.path.join(tmp, "libmsda.so")
+        tmp_lib = os.path.join(tmp, os.path.basename(lib_path))
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs,
                "-Wl,-rpath,/opt/rocm/lib"]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        shutil.copyfile(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        shutil.copyfile(tmp_lib, lib_path + ".tmp")
+        os.replace(lib_path + ".tmp", lib_path)
+    return lib_path
+
+
+def build_library(verbose: bool = False) -> str:
+    """Build libmsda.so (the library behind include/msda.h) and
+    libmsda_probe.so (cache-bandwidth probes the benchmark's roofline uses)."""
+    _build(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _build(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
