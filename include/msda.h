@@ -22,7 +22,9 @@
  * Conventions shared by every call:
  *  - Tensor pointers are DEVICE pointers to dense row-major arrays in the
  *    stated layout. The caller owns every buffer; the library allocates
- *    nothing and keeps no state between calls; calls are reentrant.
+ *    nothing and keeps no state between calls; calls are reentrant (except
+ *    msda_backward_noalloc, whose static scratch is shared by the calls on
+ *    one GPU).
  *  - Work is enqueued on `stream` (NULL = the null stream) and the call
  *    returns before it finishes. Outputs must not overlap inputs.
  *  - Every check happens on the host before the first HIP call, so an error
@@ -186,6 +188,30 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
                           void* grad_value, float* grad_sampling_locations,
                           float* grad_attention_weights, unsigned int flags, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the static device scratch msda_backward_noalloc uses in place of a workspace. */
+#define MSDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/*
+ * msda_backward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The workspace msda_backward would take is
+ * a static device array of MSDA_NOALLOC_SCRATCH_BYTES (256 MiB) inside the
+ * library; each GPU the call runs on holds its own copy from the first call
+ * on it until the process ends, and the call allocates nothing. A problem
+ * whose workspace (msda_backward_workspace_size) is larger returns
+ * MSDA_ERR_WORKSPACE_TOO_SMALL with nothing enqueued; the encoder-sized
+ * backward (2 x 22223 queries, 8 heads, 4 levels x 4 points, 32 channels)
+ * fits. `stream` must belong to the current device (else
+ * MSDA_ERR_INVALID_ARGUMENT). All calls on one GPU share its array: calls
+ * that overlap in time on one GPU (different streams, or threads) race and
+ * must be serialised by the caller. Arguments, results, determinism and the
+ * other errors are those of msda_backward.
+ */
+msda_status msda_backward_noalloc(const msda_problem* problem, const void* grad_output, const void* value,
+                                  const float* sampling_locations, const float* attention_weights,
+                                  void* grad_value, float* grad_sampling_locations,
+                                  float* grad_attention_weights, unsigned int flags, hipStream_t stream);
 
 /*
  * Producer of the sampler's inputs. For query row m = (b, q) with features

@@ -4,7 +4,7 @@
 The binding (and with it torch and the library) is loaded on first use, so the
 seeded workload generators in ``workloads`` import without a GPU.
 """
-__all__ = ["msda_forward", "msda_backward", "ms_deformable_attention", "MSDeformableAttention",
+__all__ = ["msda_forward", "msda_backward", "msda_backward_noalloc", "ms_deformable_attention", "MSDeformableAttention",
            "msda_producer_forward", "msda_fused_forward", "msda_producer_backward", "MSDAProducer",
            "load_library"]
 

@@ -36,7 +36,7 @@ ABI_VERSION = 3
 BACKWARD_ACCUMULATE_GRAD_VALUE = 1  # msda_backward flag: grad_value += result
 
 # Every symbol include/msda.h declares.
-EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
+EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size", "msda_backward_noalloc",
                     "msda_producer_forward", "msda_fused_forward", "msda_producer_backward_workspace_size",
                     "msda_producer_backward", "msda_status_string", "msda_abi_version")
 
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH):
     lib.msda_forward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     lib.msda_backward.restype = ctypes.c_int
+    lib.msda_backward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint, vp]
+    lib.msda_backward_noalloc.restype = ctypes.c_int
     lib.msda_backward_workspace_size.argtypes = [pp, ctypes.POINTER(sz)]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
     i64 = ctypes.c_int64
@@ -206,7 +208,8 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
     """Backward: returns (grad_value, grad_sampling_locations, grad_attention_weights), each in
     its input's layout, with None in the slots whose compute flag is False. With
     ``accumulate_grad_value`` the given ``grad_value`` tensor is added to instead of
-    overwritten."""
+    overwritten. ``workspace``: a GPU tensor of at least msda_backward_workspace_size
+    bytes, None (allocated here), or "static" (msda_backward_noalloc)."""
     lib = load_library()
     B, L, N_q, N_h, C_h, N_l, N_p = _dims(value, sampling_locations, value_layout,
                                           sampling_locations_layout)
@@ -239,6 +242,14 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
     prob, keep = make_problem(B, L, N_q, N_h, C_h, spatial_shapes, level_start_index, N_p,
                               value_layout, sampling_locations_layout, align_corners, padding_mode,
                               value.dtype)
+    ptr = (lambda t: None if t is None else t.data_ptr())
+    flags = BACKWARD_ACCUMULATE_GRAD_VALUE if accumulate_grad_value else 0
+    if workspace == "static":
+        st = lib.msda_backward_noalloc(ctypes.byref(prob), grad_output.data_ptr(), value.data_ptr(),
+                                       sampling_locations.data_ptr(), attention_weights.data_ptr(), ptr(gv),
+                                       ptr(gl), ptr(ga), flags, _stream_ptr(stream))
+        _raise_for(lib, st, "msda_backward_noalloc")
+        return gv, gl, ga
     ws_bytes = ctypes.c_size_t(0)
     st = lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(ws_bytes))
     _raise_for(lib, st, "msda_backward_workspace_size")
@@ -250,14 +261,28 @@ def msda_backward(grad_output, value, spatial_shapes, level_start_index, samplin
             ws = workspace
         else:
             ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=value.device)
-    ptr = (lambda t: None if t is None else t.data_ptr())
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
-    flags = BACKWARD_ACCUMULATE_GRAD_VALUE if accumulate_grad_value else 0
     st = lib.msda_backward(ctypes.byref(prob), grad_output.data_ptr(), value.data_ptr(),
                            sampling_locations.data_ptr(), attention_weights.data_ptr(), ptr(gv),
                            ptr(gl), ptr(ga), flags, ptr(ws), ws_len, _stream_ptr(stream))
     _raise_for(lib, st, "msda_backward")
     return gv, gl, ga
+
+
+def msda_backward_noalloc(grad_output, value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, value_layout="BLNC", sampling_locations_layout="BQHLP2",
+                          align_corners=False, padding_mode="zeros", compute_grad_value=True,
+                          compute_grad_sampling_locations=True, compute_grad_attention_weights=True,
+                          grad_value=None, grad_sampling_locations=None, grad_attention_weights=None,
+                          accumulate_grad_value=False, stream=None):
+    """msda_backward with its workspace in the library's static device scratch
+    (for callers that cannot allocate: pass every output tensor). Raises if the
+    problem needs more than that scratch holds."""
+    return msda_backward(grad_output, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, value_layout, sampling_locations_layout, align_corners,
+                         padding_mode, compute_grad_value, compute_grad_sampling_locations,
+                         compute_grad_attention_weights, grad_value, grad_sampling_locations,
+                         grad_attention_weights, accumulate_grad_value, workspace="static", stream=stream)
 
 
 class MSDeformableAttention(torch.autograd.Function):

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/msda.h"
 #include "msda_device.h"
@@ -363,6 +364,128 @@ msda::ProducerArgsRaw producer_args(const void* query, const float* ref, const v
     return msda::ProducerArgsRaw{query, ref, w_off, b_off, w_att, b_att};
 }
 
+// msda_backward's validation and dispatch. With need_out, nothing is launched:
+// every check except the workspace's runs, and *need_out receives the bytes
+// of workspace the call would use.
+msda_status backward_call(const msda_problem* problem, const void* grad_output, const void* value,
+                          const float* sampling_locations, const float* attention_weights, void* grad_value,
+                          float* grad_sampling_locations, float* grad_attention_weights, unsigned int flags,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, size_t* need_out)
+{
+    if (need_out) *need_out = 0;
+    Geometry g;
+    Sizes z;
+    const msda_status st = check_problem(problem, &g, &z);
+    if (st != MSDA_OK) return st;
+    if (flags & ~(unsigned int)MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) return MSDA_ERR_INVALID_ARGUMENT;
+    const int accumulate = (flags & MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) ? 1 : 0;
+    if (!grad_value && !grad_sampling_locations && !grad_attention_weights) return MSDA_ERR_NOTHING_TO_COMPUTE;
+    const bool empty = z.out_elems == 0;
+    const bool bf16 = problem->value_dtype == MSDA_BF16;
+    if (!empty && (!grad_output || !value || !sampling_locations || !attention_weights))
+        return MSDA_ERR_INVALID_ARGUMENT;
+    const void* ins[4] = {grad_output, value, sampling_locations, attention_weights};
+    const size_t in_align[4] = {(size_t)z.elem, (size_t)z.elem, 4, 4};
+    for (int i = 0; i < 4; ++i)
+        if (ins[i] && !aligned(ins[i], in_align[i])) return MSDA_ERR_INVALID_ARGUMENT;
+    const void* outs[3] = {grad_value, grad_sampling_locations, grad_attention_weights};
+    const size_t out_align[3] = {(size_t)z.elem, 4, 4};
+    for (int o = 0; o < 3; ++o)
+        if (outs[o] && !aligned(outs[o], out_align[o])) return MSDA_ERR_INVALID_ARGUMENT;
+    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
+    const size_t in_bytes[4] = {z.out_bytes, z.value_bytes, loc_bytes, attn_bytes};
+    const size_t out_bytes[3] = {z.value_bytes, loc_bytes, attn_bytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return MSDA_ERR_INVALID_ARGUMENT;
+    }
+
+    // Fast path: 4 channels per lane (one 16-byte float32 or 8-byte bfloat16
+    // load) and the destination-tiled grad_value pass; otherwise one channel
+    // per lane and atomics.
+    const int64_t C_h = problem->C_h;
+    const size_t row_align = 4 * (size_t)z.elem;
+    TilePlan tp = {};
+    const bool fast = fast_backward_shape(*problem) && plan_tiles(*problem, fast_lanes(C_h), &tp) &&
+                      aligned(value, row_align) && aligned(grad_output, row_align) &&
+                      (!grad_value || aligned(grad_value, row_align));
+    if (grad_value && !empty) {
+        const size_t need = fast ? msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr, nullptr)
+                                 : generic_workspace_bytes(*problem, z);
+        if (need_out) *need_out = need;
+        if (need > 0 && !need_out) {
+            if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
+            if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
+            for (int i = 0; i < 4; ++i)
+                if (overlap(workspace, need, ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
+            for (int o = 0; o < 3; ++o)
+                if (overlap(workspace, need, outs[o], out_bytes[o])) return MSDA_ERR_INVALID_ARGUMENT;
+        }
+    }
+    const int lpu = fast ? fast_lanes(C_h) : 1 << ilog2((int)std::min<int64_t>(64, C_h));
+    const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
+    const int64_t upb = msda::kBlock / lpu;
+    g.lpu_log2 = ilog2(lpu);
+    g.chunks = 1;
+    g.units = (int32_t)units;
+    g.blocks = (int32_t)((units + upb - 1) / upb);
+    g.loc_pair_aligned = aligned(sampling_locations, 8) && (!grad_sampling_locations || aligned(grad_sampling_locations, 8));
+    if (fast && grad_value && !empty && (int64_t)tp.jobs * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    if (need_out) return MSDA_OK;
+
+    hipError_t e = hipSuccess;
+    if (empty) {
+        // no query reaches grad_value: it is all zeros (or left as is)
+        if (grad_value && !accumulate) e = msda::launch_zero_elems(grad_value, z.value_elems, z.elem, stream);
+        return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+    }
+    if (fast) {
+        e = msda::launch_backward_fast(g, tp, lpu, bf16, accumulate, grad_output, value, sampling_locations,
+                                       attention_weights, grad_value, grad_sampling_locations,
+                                       grad_attention_weights, workspace, stream);
+    } else {
+        e = msda::launch_backward_generic(g, lpu, bf16, accumulate, grad_output, value, sampling_locations,
+                                          attention_weights, grad_value, grad_sampling_locations,
+                                          grad_attention_weights, workspace, stream);
+    }
+    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
+// Static scratch of msda_backward_noalloc: the workspace msda_backward would
+// take, as a device array of the library. Each GPU holds its own copy (at its
+// own address) from the module's load until the process ends. Host code never
+// uses the array's name as an address: it takes each device's address from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)MSDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address; `stream` (if not NULL) must belong to the
+// current device.
+msda_status scratch_for_current_device(hipStream_t stream, void** ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MSDA_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MSDA_ERR_HIP;
+        if ((int)sdev != dev) return MSDA_ERR_INVALID_ARGUMENT;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MSDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSDA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MSDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,82 +543,30 @@ msda_status msda_backward(const msda_problem* problem, const void* grad_output, 
                           float* grad_sampling_locations, float* grad_attention_weights, unsigned int flags,
                           void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    Geometry g;
-    Sizes z;
-    const msda_status st = check_problem(problem, &g, &z);
+    return backward_call(problem, grad_output, value, sampling_locations, attention_weights, grad_value,
+                         grad_sampling_locations, grad_attention_weights, flags, workspace, workspace_bytes, stream,
+                         nullptr);
+}
+
+msda_status msda_backward_noalloc(const msda_problem* problem, const void* grad_output, const void* value,
+                                  const float* sampling_locations, const float* attention_weights, void* grad_value,
+                                  float* grad_sampling_locations, float* grad_attention_weights, unsigned int flags,
+                                  hipStream_t stream)
+{
+    // every check first, without a HIP call; then this device's scratch
+    size_t need = 0;
+    msda_status st = backward_call(problem, grad_output, value, sampling_locations, attention_weights, grad_value,
+                                   grad_sampling_locations, grad_attention_weights, flags, nullptr, 0, stream, &need);
     if (st != MSDA_OK) return st;
-    if (flags & ~(unsigned int)MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) return MSDA_ERR_INVALID_ARGUMENT;
-    const int accumulate = (flags & MSDA_BACKWARD_ACCUMULATE_GRAD_VALUE) ? 1 : 0;
-    if (!grad_value && !grad_sampling_locations && !grad_attention_weights) return MSDA_ERR_NOTHING_TO_COMPUTE;
-    const bool empty = z.out_elems == 0;
-    const bool bf16 = problem->value_dtype == MSDA_BF16;
-    if (!empty && (!grad_output || !value || !sampling_locations || !attention_weights))
-        return MSDA_ERR_INVALID_ARGUMENT;
-    const void* ins[4] = {grad_output, value, sampling_locations, attention_weights};
-    const size_t in_align[4] = {(size_t)z.elem, (size_t)z.elem, 4, 4};
-    for (int i = 0; i < 4; ++i)
-        if (ins[i] && !aligned(ins[i], in_align[i])) return MSDA_ERR_INVALID_ARGUMENT;
-    const void* outs[3] = {grad_value, grad_sampling_locations, grad_attention_weights};
-    const size_t out_align[3] = {(size_t)z.elem, 4, 4};
-    for (int o = 0; o < 3; ++o)
-        if (outs[o] && !aligned(outs[o], out_align[o])) return MSDA_ERR_INVALID_ARGUMENT;
-    const size_t loc_bytes = (size_t)z.loc_elems * 4, attn_bytes = (size_t)z.attn_elems * 4;
-    const size_t in_bytes[4] = {z.out_bytes, z.value_bytes, loc_bytes, attn_bytes};
-    const size_t out_bytes[3] = {z.value_bytes, loc_bytes, attn_bytes};
-    for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 4; ++i)
-            if (overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
-        for (int o2 = o + 1; o2 < 3; ++o2)
-            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return MSDA_ERR_INVALID_ARGUMENT;
+    if (need > kNoAllocScratchBytes) return MSDA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_for_current_device(stream, &ws);
+        if (st != MSDA_OK) return st;
     }
-
-    // Fast path: 4 channels per lane (one 16-byte float32 or 8-byte bfloat16
-    // load) and the destination-tiled grad_value pass; otherwise one channel
-    // per lane and atomics.
-    const int64_t C_h = problem->C_h;
-    const size_t row_align = 4 * (size_t)z.elem;
-    TilePlan tp = {};
-    const bool fast = fast_backward_shape(*problem) && plan_tiles(*problem, fast_lanes(C_h), &tp) &&
-                      aligned(value, row_align) && aligned(grad_output, row_align) &&
-                      (!grad_value || aligned(grad_value, row_align));
-    if (grad_value && !empty) {
-        const size_t need = fast ? msda::fast_workspace_layout(g, tp, nullptr, nullptr, nullptr, nullptr)
-                                 : generic_workspace_bytes(*problem, z);
-        if (need > 0) {
-            if (!workspace || workspace_bytes < need) return MSDA_ERR_WORKSPACE_TOO_SMALL;
-            if (!aligned(workspace, 16)) return MSDA_ERR_INVALID_ARGUMENT;
-            for (int i = 0; i < 4; ++i)
-                if (overlap(workspace, need, ins[i], in_bytes[i])) return MSDA_ERR_INVALID_ARGUMENT;
-            for (int o = 0; o < 3; ++o)
-                if (overlap(workspace, need, outs[o], out_bytes[o])) return MSDA_ERR_INVALID_ARGUMENT;
-        }
-    }
-    const int lpu = fast ? fast_lanes(C_h) : 1 << ilog2((int)std::min<int64_t>(64, C_h));
-    const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
-    const int64_t upb = msda::kBlock / lpu;
-    g.lpu_log2 = ilog2(lpu);
-    g.chunks = 1;
-    g.units = (int32_t)units;
-    g.blocks = (int32_t)((units + upb - 1) / upb);
-    g.loc_pair_aligned = aligned(sampling_locations, 8) && (!grad_sampling_locations || aligned(grad_sampling_locations, 8));
-    if (fast && grad_value && !empty && (int64_t)tp.jobs * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
-
-    hipError_t e = hipSuccess;
-    if (empty) {
-        // no query reaches grad_value: it is all zeros (or left as is)
-        if (grad_value && !accumulate) e = msda::launch_zero_elems(grad_value, z.value_elems, z.elem, stream);
-        return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
-    }
-    if (fast) {
-        e = msda::launch_backward_fast(g, tp, lpu, bf16, accumulate, grad_output, value, sampling_locations,
-                                       attention_weights, grad_value, grad_sampling_locations,
-                                       grad_attention_weights, workspace, stream);
-    } else {
-        e = msda::launch_backward_generic(g, lpu, bf16, accumulate, grad_output, value, sampling_locations,
-                                          attention_weights, grad_value, grad_sampling_locations,
-                                          grad_attention_weights, workspace, stream);
-    }
-    return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+    return backward_call(problem, grad_output, value, sampling_locations, attention_weights, grad_value,
+                         grad_sampling_locations, grad_attention_weights, flags, ws, ws ? kNoAllocScratchBytes : 0,
+                         stream, nullptr);
 }
 
 msda_status msda_producer_forward(const msda_problem* problem, int64_t D, const void* query,

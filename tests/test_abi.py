@@ -318,3 +318,35 @@ def test_producer_workspace_size(lib):
     assert sz.value % per_chunk == 0
     chunks = sz.value // per_chunk
     assert 16 <= chunks <= 64 and chunks * 32 >= M // 64
+
+
+# ------------------------------------------------------------ no-alloc ---
+
+def _bwd_noalloc(lib, prob, gv=P["gv"], gl=P["gl"], ga=P["ga"], gout=P["gout"], value=P["value"], flags=0):
+    return lib.msda_backward_noalloc(ctypes.byref(prob), gout, value, P["loc"], P["attn"], gv, gl, ga, flags, None)
+
+
+def test_noalloc_validates_like_msda_backward(lib):
+    prob, keep = _prob()
+    assert _bwd_noalloc(lib, prob, gv=None, gl=None, ga=None) == 3
+    assert _bwd_noalloc(lib, prob, flags=2) == 1
+    assert _bwd_noalloc(lib, prob, gl=ctypes.c_void_p(P["value"].value + 128)) == 1
+    assert _bwd_noalloc(lib, prob, value=None) == 1
+    prob.N_h = 0
+    assert _bwd_noalloc(lib, prob) == 1
+
+
+def test_noalloc_rejects_problems_past_its_scratch(lib):
+    # 4 x 22223 encoder queries need about twice the 256 MiB static scratch:
+    # rejected on the host, nothing enqueued
+    levels = ((100, 167), (50, 84), (25, 42), (13, 21))
+    starts = (0, 16700, 20900, 21950)
+    prob, keep = binding.make_problem(4, 22223, 22223, 8, 32, levels, starts, 4)
+    sz = ctypes.c_size_t(0)
+    assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
+    assert sz.value > 256 << 20
+    assert _bwd_noalloc(lib, prob) == 5
+    # the encoder-sized problem itself fits
+    prob, keep = binding.make_problem(2, 22223, 22223, 8, 32, levels, starts, 4)
+    assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
+    assert sz.value <= 256 << 20
