@@ -330,7 +330,6 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const int tid = threadIdx.x;
     const int u0 = xcd_logical_block(blockIdx.x, gridDim.x) * upb;
     const bool want_dots = grad_loc != nullptr || grad_attn != nullptr;
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
     const __amdgpu_buffer_rsrc_t vr = value_rsrc(value, BUF ? value_bytes : 0);
 
     const int grp = tid / LPU, lig = tid % LPU;
