@@ -408,7 +408,8 @@ def report(a):
                 "queries_per_s": bc["queries"] / avg_s,
                 "gbs_counted": bc[name]["counted"] / avg_s / 1e9,
                 "gbs_nominal": bc[name]["nominal"] / avg_s / 1e9,
-                "frac_of_hbm_peak_counted": bc[name]["counted"] / avg_s / 1e9 / HBM_PEAK_GBS,
+                "l2_frac_counted": bc[name]["counted"] / avg_s / 1e9 / L2_PEAK_GBS,
+                "effective_gbs_vs_hbm_peak": bc[name]["counted"] / avg_s / 1e9 / HBM_PEAK_GBS,
             }
         if not a.no_cpu_baseline:
             for name in ("forward", "backward"):
