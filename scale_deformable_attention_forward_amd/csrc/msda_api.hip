@@ -174,7 +174,11 @@ bool fast_backward_shape(const msda_problem& p)
     return true;
 }
 
-// Cut every level into bands (destination tiles) of rows x cols pixels. The
+// Cut every level into bands (destination tiles) of rows x cols pixels.
+// Levels with fewer samples per slab than pixels take pixel mode: bands of
+// at most kTileBins anchor bins expected to hold about three quarters of
+// one LDS pass of entries, fewest bands first, walked by lane groups that
+// own pixel blocks. Every other level takes halo mode: the
 // (rows + 1) x (cols + 1) anchor bins of a band are dealt out to ny x nx lane
 // groups in blocks of kRectRows x RW bins (ny * nx <= the groups of one tile
 // workgroup), so rows = ny * kRectRows - 1 and cols = nx * RW - 1 (or the
@@ -214,15 +218,37 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         tp->rpieces_per_band[l] = 1;
         tp->rows_div[l] = msda::make_fastdiv(1);
         tp->cols_div[l] = msda::make_fastdiv(1);
+        tp->mode[l] = msda::kTileHalo;
         if (l >= p.N_l) {
             tp->rows[l] = tp->row_bands[l] = tp->cols[l] = tp->col_bands[l] = tp->chunks[l] = 1;
             continue;
         }
         const int64_t H = p.spatial_shapes[2 * l], W = p.spatial_shapes[2 * l + 1];
-        // a band of r x c pixels has (r + 1) x (c + 1) anchor bins, dealt out
-        // to ny x nx lane groups in blocks of RH x RW bins
         int64_t rows = 0, cols = 0, rb = 0, cb = 0;
-        const int64_t nx_max = std::min<int64_t>(groups, W / RW + 1);
+        tp->mode[l] = msda::kTileHalo;
+        if (nsamp > 0 && nsamp < H * W) {
+            // pixel mode: bands of at most kTileBins anchor bins holding about
+            // three quarters of a pass of entries if locations spread evenly
+            // (so one pass is the rule), fewest bands, then fewest column bands
+            const int64_t r_max = std::min<int64_t>(H, msda::kTileBins / 2 - 1);
+            for (int64_t r = 1; r <= r_max; ++r) {
+                const int64_t c_bins = msda::kTileBins / (r + 1) - 1;
+                const int64_t c_fill = 3 * msda::kTileEntries / 4 * (H + 1) * (W + 1) / (nsamp * (r + 1)) - 1;
+                const int64_t c = std::min<int64_t>(W, std::min(c_bins, c_fill));
+                if (c < 1) continue;
+                const int64_t nrb = (H + r - 1) / r, ncb = (W + c - 1) / c;
+                if (rows == 0 || nrb * ncb < rb * cb || (nrb * ncb == rb * cb && ncb < cb)) {
+                    rows = r;
+                    cols = c;
+                    rb = nrb;
+                    cb = ncb;
+                }
+            }
+            if (rows > 0) tp->mode[l] = msda::kTilePixel;
+        }
+        // halo mode: a band of r x c pixels has (r + 1) x (c + 1) anchor bins,
+        // dealt out to ny x nx lane groups in blocks of RH x RW bins
+        const int64_t nx_max = tp->mode[l] == msda::kTilePixel ? 0 : std::min<int64_t>(groups, W / RW + 1);
         for (int64_t nx = 1; nx <= nx_max; ++nx) {
             const int64_t ny = std::min<int64_t>(groups / nx, H / RH + 1);
             const int64_t r = std::min<int64_t>(H, ny * RH - 1), c = std::min<int64_t>(W, nx * RW - 1);
@@ -241,6 +267,7 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;
         int64_t chunks = (expect + 3 * msda::kTileEntries - 1) / (3 * msda::kTileEntries);
         chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, std::min<int64_t>(nwg, 1024)));  // >= 1 run each
+        if (tp->mode[l] == msda::kTilePixel) chunks = 1;  // pixel-mode bands are not split
         tp->rows[l] = (int32_t)rows;
         tp->rows_div[l] = msda::make_fastdiv((uint32_t)rows);
         tp->cols_div[l] = msda::make_fastdiv((uint32_t)cols);

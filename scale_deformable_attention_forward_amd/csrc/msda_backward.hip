@@ -416,14 +416,14 @@ struct BandWs {
 };
 
 struct LevelTiles {
-    int H, W, start, R, CW, nbr, nbc, nch, band0, job0, part;
+    int H, W, start, R, CW, nbr, nbc, nch, band0, job0, part, mode;
     FastDiv rd, cd;  // by R, by CW
 };
 
 // Tile geometry of level l (static indices only, so the plan stays in kernel-argument memory).
 __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TilePlan& tp, int l)
 {
-    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, make_fastdiv(1), make_fastdiv(1)};
+    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, 0, make_fastdiv(1), make_fastdiv(1)};
 #pragma unroll
     for (int k = 0; k < kMaxLevels; ++k) {
         if (k == l) {
@@ -438,6 +438,7 @@ __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TileP
             t.band0 = tp.band_begin[k];
             t.job0 = tp.job_begin[k];
             t.part = tp.part_off[k];
+            t.mode = tp.mode[k];
             t.rd = tp.rows_div[k];
             t.cd = tp.cols_div[k];
         }
@@ -630,19 +631,250 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
     VecIO<T, 4>::store(dst, v);
 }
 
-// Tile kernel. LPU lanes per lane group (4 channels per lane). The band's
-// anchor bins (anchor rows r0-1..r1-1, columns c0-1..c1-1) are dealt out to
-// the kTileBlock / LPU groups in blocks of kRectRows x RW bins. An entry
-// anchored at (x0, y0) reaches the pixels (x0..x0+1, y0..y0+1), so a
-// group's block of bins reaches (kRectRows + 1) x (RW + 1) pixels: its own
-// kRectRows x RW and a halo row above and column to the left,
-// which belong to the neighbouring groups. Every entry's grad_output row is
-// thus loaded once and applied to all four corners; after the walk the
-// groups hand their halos to their neighbours through LDS, which add them in
-// a fixed order.
+// Tile kernel. LPU lanes per lane group (4 channels per lane). A job takes
+// one band (or one chunk of a split band's list). Entries are staged in LDS
+// a pass at a time (whole runs, at most kTileEntries entries) in (anchor
+// bin, k) order. An entry anchored at (x0, y0) reaches the pixels
+// (x0..x0+1, y0..y0+1). Two ways of walking the bins, chosen per level:
+//  - halo mode (levels with at least as many samples as pixels): the band's
+//    anchor bins (anchor rows r0-1..r1-1, columns c0-1..c1-1) are dealt out
+//    to the kTileBlock / LPU groups in blocks of kRectRows x RW bins; a
+//    group's block reaches (kRectRows + 1) x (RW + 1) pixels: its own
+//    kRectRows x RW and a halo row above and column to the left, which
+//    belong to the neighbouring groups. Every entry's grad_output row is
+//    thus loaded once and applied to all four corners; after the passes the
+//    groups hand their halos to their neighbours through LDS, which add
+//    them in a fixed order;
+//  - pixel mode (levels with fewer samples than pixels): bands are as large
+//    as the bin table allows and every group owns blocks of kRectRows x
+//    kPixCols pixels, one block per round, walking the (kRectRows + 1) x
+//    (kPixCols + 1) bins around it and keeping only the corners that fall in
+//    its block. An entry's row is loaded by every group it reaches (up to
+//    four), but there is no halo exchange, and a band of one pass is staged
+//    once for all its rounds, so the per-job work shrinks for sparse levels.
 // Byte offset past the end of every grad_output buffer the tile kernel reads
 // (buffer spans stay below 2^31 bytes): such a load returns zeros.
 constexpr uint32_t kNoRowBytes = 1u << 31;
+
+// LDS of one tile workgroup.
+struct TileLds {
+    // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
+    // A fy (1-fx), A fy fx and the element offset q * N_h * C_h of the
+    // grad_output row; the three slots after a pass's last entry hold zeros
+    float4 w[kTileEntries + 3];
+    uint32_t row[kTileEntries + 3];
+    uint32_t bkey[kTileEntries];     // sample indices k in binned order
+    int bstart[kTileBins + 1];       // bin boundaries in w / row
+    int cursor[kTileBins];
+    int wave[kTileBlock / kWave];
+};
+
+// The pass that starts at run wr of a job: its end run wn (the pass ends
+// before the first run that would overflow kTileEntries entries), its first
+// list offset p0 and entry count m. Run ends never decrease, so the lanes
+// test 64 runs per load instead of walking them one dependent load at a time.
+__device__ __forceinline__ void find_pass(const int* run_off, int wr, int w_hi, int& wn, int& p0, int& m)
+{
+    p0 = run_off[wr];
+    wn = wr + 1;
+    while (wn < w_hi) {
+        const int w = wn + (int)(threadIdx.x % kWave);
+        const uint64_t fits = __ballot(w < w_hi && run_off[w + 1] - p0 <= kTileEntries);
+        if (~fits == 0) {
+            wn += kWave;
+            continue;
+        }
+        wn += __ffsll((unsigned long long)~fits) - 1;
+        break;
+    }
+    m = run_off[wn] - p0;
+}
+
+// Stage one pass (m_cnt list entries from offset p0) of a band whose anchor
+// bins are rows r0-1.., columns c0-1.. (nbw bins a row, nbins in all): count
+// the entries per bin, scan, place the sample indices in their bins, rank
+// each entry among its bin by k (keys are unique within a band list) and
+// write its corner weights and grad_output row offset to its place.
+// Every thread takes part; ends with a barrier.
+__device__ __forceinline__ void stage_pass(TileLds& s, const Geometry& g, const uint32_t* __restrict__ list,
+                                           const float4* __restrict__ srec, int p0, int m_cnt, int r0, int c0,
+                                           int nbw, int nbins, int gq)
+{
+    constexpr int kWaves = kTileBlock / kWave;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < nbins; i += kTileBlock) s.cursor[i] = 0;
+    __syncthreads();
+    // (each thread keeps its entries' sample indices, bins and records in
+    // registers until it writes them to LDS in their sorted place)
+    constexpr int kStage = kTileEntries / kTileBlock;
+    uint32_t kk[kStage];
+    int bn[kStage];
+    float rfx[kStage], rfy[kStage], ra[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kTileBlock;
+        kk[u] = i < m_cnt ? __builtin_nontemporal_load(list + p0 + i) : 0u;  // read once
+    }
+    // each entry's record (anchor corner, fractions, attention weight) as
+    // the backward kernel wrote it (read about once)
+    f32x4_t rc[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        rc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (tid + u * kTileBlock < m_cnt)
+            rc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(srec + kk[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kTileBlock;
+        if (i >= m_cnt) continue;
+        int x0, y0;
+        unpack_anchor(__float_as_uint(rc[u].x), x0, y0);
+        rfx[u] = rc[u].y;
+        rfy[u] = rc[u].z;
+        ra[u] = rc[u].w;
+        bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
+        atomicAdd(&s.cursor[bn[u]], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the bin counts into the bin starts and the placement
+    // cursors: each thread adds up to kBinsPerThread consecutive counts, one
+    // block-wide scan of those sums
+    {
+        constexpr int kBinsPerThread = (kTileBins + kTileBlock - 1) / kTileBlock;
+        const int per = (nbins + kTileBlock - 1) / kTileBlock;
+        const int i0 = tid * per;
+        int v[kBinsPerThread];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kBinsPerThread; ++j) {
+            v[j] = j < per && i0 + j < nbins ? s.cursor[i0 + j] : 0;
+            sum += v[j];
+        }
+        const int lane = tid % kWave, wave = tid / kWave;
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int u = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += u;
+        }
+        if (lane == kWave - 1) s.wave[wave] = incl;
+        __syncthreads();
+        int run = incl - sum;
+        for (int ww = 0; ww < wave; ++ww) run += s.wave[ww];
+#pragma unroll
+        for (int j = 0; j < kBinsPerThread; ++j) {
+            if (j < per && i0 + j < nbins) {
+                s.bstart[i0 + j] = run;
+                s.cursor[i0 + j] = run;
+            }
+            run += v[j];
+        }
+        if (tid == kTileBlock - 1) {
+            int tot = 0;
+            for (int ww = 0; ww < kWaves; ++ww) tot += s.wave[ww];
+            s.bstart[nbins] = tot;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStage; ++u)
+        if (tid + u * kTileBlock < m_cnt) s.bkey[atomicAdd(&s.cursor[bn[u]], 1)] = kk[u];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kTileBlock;
+        if (i >= m_cnt) continue;
+        const uint32_t key = kk[u];
+        const int b0 = s.bstart[bn[u]], b1 = s.bstart[bn[u] + 1];
+        int rank = 0;
+        for (int j = b0; j < b1; ++j) rank += s.bkey[j] < key ? 1 : 0;
+        const int q = fdiv((int)key, g.np_div);
+        const float fx = rfx[u], fy = rfy[u], A = ra[u];
+        const float a0 = A * (1.f - fy), a1 = A * fy;
+        s.w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
+        s.row[b0 + rank] = (uint32_t)(q * gq);
+    }
+    if (tid < 3) {
+        s.w[m_cnt + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s.row[m_cnt + tid] = 0u;
+    }
+    __syncthreads();
+}
+
+// Terms of four entries of one bin for the pixels of a group's accumulator
+// window: corner (dx, dy) of an entry in window bin (bi, bj) is window
+// pixel (bi - 1 + dy + OY, bj - 1 + dx + OX) (OY = OX = 1 in halo mode,
+// where window row and column 0 are the halo; 0 in pixel mode); corners
+// outside the window are dropped. The four entries' terms are summed before
+// they join the pixel's total, which keeps float32 rounding chains short.
+template <int WR, int WC, int OY, int OX>
+__device__ __forceinline__ void add_bin_terms(float4 (&acc)[WR][WC], int bi, int bj, const float4 (&wv)[4],
+                                              const float (&gv)[4][4])
+{
+#pragma unroll
+    for (int dy = 0; dy < 2; ++dy) {
+        const int pr = bi - 1 + dy + OY;
+        if (pr < 0 || pr >= WR) continue;
+#pragma unroll
+        for (int dx = 0; dx < 2; ++dx) {
+            const int pc = bj - 1 + dx + OX;
+            if (pc < 0 || pc >= WC) continue;
+            float4 ts;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 w4 = wv[u];
+                const float wc = dy ? (dx ? w4.w : w4.z) : (dx ? w4.y : w4.x);
+                if (u == 0) {
+                    ts = make_float4(wc * gv[u][0], wc * gv[u][1], wc * gv[u][2], wc * gv[u][3]);
+                } else {
+                    ts.x = __builtin_fmaf(wc, gv[u][0], ts.x);
+                    ts.y = __builtin_fmaf(wc, gv[u][1], ts.y);
+                    ts.z = __builtin_fmaf(wc, gv[u][2], ts.z);
+                    ts.w = __builtin_fmaf(wc, gv[u][3], ts.w);
+                }
+            }
+            acc[pr][pc].x += ts.x;
+            acc[pr][pc].y += ts.y;
+            acc[pr][pc].z += ts.z;
+            acc[pr][pc].w += ts.w;
+        }
+    }
+}
+
+// Walk bins (by0 + bi, bx0 + bj), bi < BR, bj < BC, of the staged pass
+// (bins past the band's th x tw pixels are empty), four entries at a time:
+// their grad_output rows are loaded (slots past a bin's end load no row: the
+// buffer returns zeros past its end, so whatever weights they read add
+// nothing) and their terms added to the window.
+template <typename T, int BR, int BC, int WR, int WC, int OY, int OX>
+__device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc_t gr, int ch, int by0, int bx0,
+                                          int th, int tw, int nbw, float4 (&acc)[WR][WC])
+{
+#pragma unroll
+    for (int bi = 0; bi < BR; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < BC; ++bj) {
+            const int by = by0 + bi, bx = bx0 + bj;
+            int e0 = 0, e1 = 0;
+            if (by <= th && bx <= tw) {
+                e0 = s.bstart[by * nbw + bx];
+                e1 = s.bstart[by * nbw + bx + 1];
+            }
+            for (int e = e0; e < e1; e += 4) {
+                float4 wv[4];
+                float gv[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    wv[u] = s.w[e + u];
+                    const uint32_t row = s.row[e + u];
+                    BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
+                }
+                add_bin_terms<WR, WC, OY, OX>(acc, bi, bj, wv, gv);
+            }
+        }
+    }
+}
 
 template <typename T, int LPU, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
@@ -651,16 +883,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 {
     constexpr int RH = kRectRows;
     constexpr int E = kTileEntries;
-    constexpr int kWaves = kTileBlock / kWave;
-    // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
-    // A fy (1-fx), A fy fx and the element offset q * N_h * C_h of the
-    // grad_output row; the three slots after a pass's last entry hold zeros
-    __shared__ float4 s_w[E + 3];
-    __shared__ uint32_t s_row[E + 3];
-    __shared__ uint32_t s_bkey[E];           // sample indices k in binned order
-    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_w / s_row
-    __shared__ int s_cursor[kTileBins];
-    __shared__ int s_wave[kWaves];
+    __shared__ TileLds s;
 
     const int tid = threadIdx.x;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -685,15 +908,63 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // this chunk's runs [w_lo, w_hi) of the band's list; run_off[w] is where run w starts
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
-    const size_t lbase = (size_t)slab * tp.cap;
+    const uint32_t* list = w.k + (size_t)slab * tp.cap;
     const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
     // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
     const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, (int64_t)g.Nq * gq * (int64_t)sizeof(T));
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;  // + pixel * pstride
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
+
+    if (t.mode == kTilePixel) {
+        // ---- pixel mode: rounds of kRectRows x kPixCols pixel blocks ----
+        constexpr int PC = kPixCols;
+        constexpr int kGroups = kTileBlock / LPU;
+        const int pbw = (tw + PC - 1) / PC, nblk = ((th + RH - 1) / RH) * pbw;
+        int wn, p0, m_cnt;
+        find_pass(run_off, w_lo, w_hi, wn, p0, m_cnt);
+        const bool single = wn >= w_hi;  // one pass: staged once for every round
+        if (single) stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
+        for (int rb = 0; rb < nblk; rb += kGroups) {
+            const int blk = rb + grp;
+            const bool own = blk < nblk && ch < g.Ch;
+            const int pby = own ? blk / pbw : 0, pbx = own ? blk - (blk / pbw) * pbw : 0;
+            const int py0 = pby * RH, px0 = pbx * PC;  // the block's first pixel, band-local
+            float4 acc[RH][PC];
+#pragma unroll
+            for (int i = 0; i < RH; ++i)
+#pragma unroll
+                for (int j = 0; j < PC; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int wr = w_lo; wr < w_hi;) {
+                if (!single) {
+                    find_pass(run_off, wr, w_hi, wn, p0, m_cnt);
+                    stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
+                }
+                // bins py0..py0+RH, px0..px0+PC reach the block (bin (by, bx)
+                // is anchored at band-local pixel (by - 1, bx - 1))
+                if (own) walk_bins<T, RH + 1, PC + 1, RH, PC, 0, 0>(s, gr, ch, py0, px0, th, tw, nbw, acc);
+                if (!single) __syncthreads();  // the next pass is staged over this one
+                wr = wn;
+            }
+            if (own) {
+#pragma unroll
+                for (int i = 0; i < RH; ++i)
+#pragma unroll
+                    for (int j = 0; j < PC; ++j) {
+                        const int py = py0 + i, px = px0 + j;
+                        if (py < th && px < tw)
+                            store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[i][j], accumulate);
+                    }
+            }
+        }
+        return;
+    }
+
+    // ---- halo mode ----
     const int gnx = (tw + RW) / RW, gny = (th + RH) / RH;  // group blocks cover the (th+1) x (tw+1) bins
     const int gy = grp / gnx, gx = grp - gy * gnx;
     const int by0 = gy * RH, bx0 = gx * RW;  // the group's first bin (bin row 0 is anchor row r0 - 1)
@@ -712,185 +983,22 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // order inside runs; inside a pass every bin is summed in k order. The
     // sums are therefore the same on every call.
     for (int wr = w_lo; wr < w_hi;) {
-        const int p0 = run_off[wr];
-        // the pass ends before the first run that would overflow E entries;
-        // run ends never decrease, so the lanes test 64 runs per load instead
-        // of walking them one dependent load at a time
-        int wn = wr + 1;
-        while (wn < w_hi) {
-            const int w = wn + tid % kWave;
-            const uint64_t fits = __ballot(w < w_hi && run_off[w + 1] - p0 <= E);
-            if (~fits == 0) {
-                wn += kWave;
-                continue;
-            }
-            wn += __ffsll((unsigned long long)~fits) - 1;
-            break;
-        }
-        const int m_cnt = run_off[wn] - p0;
+        int wn, p0, m_cnt;
+        find_pass(run_off, wr, w_hi, wn, p0, m_cnt);
         wr = wn;
-        // stage a pass of list entries and count them per anchor bin
-        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
-        __syncthreads();
-        // (each thread keeps its entries' sample indices, bins and records in
-        // registers until it writes them to LDS in their sorted place)
-        constexpr int kStage = kTileEntries / kTileBlock;
-        uint32_t kk[kStage];
-        int bn[kStage];
-        float rfx[kStage], rfy[kStage], ra[kStage];
-#pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            const int i = tid + u * kTileBlock;
-            kk[u] = i < m_cnt ? __builtin_nontemporal_load(w.k + lbase + p0 + i) : 0u;  // read once
-        }
-        // each entry's record (anchor corner, fractions, attention weight) as
-        // the backward kernel wrote it (read about once)
-        f32x4_t rc[kStage];
-#pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            rc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (tid + u * kTileBlock < m_cnt)
-                rc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(srec + kk[u]));
-        }
-#pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            const int i = tid + u * kTileBlock;
-            if (i >= m_cnt) continue;
-            int x0, y0;
-            unpack_anchor(__float_as_uint(rc[u].x), x0, y0);
-            rfx[u] = rc[u].y;
-            rfy[u] = rc[u].z;
-            ra[u] = rc[u].w;
-            bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
-            atomicAdd(&s_cursor[bn[u]], 1);
-        }
-        __syncthreads();
-        // exclusive scan of the bin counts
-        for (int base = 0; base < nbins; base += kTileBlock) {
-            const int i = base + tid;
-            const int v = i < nbins ? s_cursor[i] : 0;
-            int incl = v;
-            const int lane = tid % kWave, wave = tid / kWave;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const int u = __shfl_up(incl, d, kWave);
-                if (lane >= d) incl += u;
-            }
-            if (lane == kWave - 1) s_wave[wave] = incl;
-            __syncthreads();
-            int before = base == 0 ? 0 : s_bstart[base];
-            for (int ww = 0; ww < wave; ++ww) before += s_wave[ww];
-            if (i < nbins) s_bstart[i] = before + incl - v;
-            if (tid == kTileBlock - 1) {
-                int tot = base == 0 ? 0 : s_bstart[base];
-                for (int ww = 0; ww < kWaves; ++ww) tot += s_wave[ww];
-                s_bstart[min(base + kTileBlock, nbins)] = tot;
-            }
-            __syncthreads();
-        }
-        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < kStage; ++u)
-            if (tid + u * kTileBlock < m_cnt) s_bkey[atomicAdd(&s_cursor[bn[u]], 1)] = kk[u];
-        __syncthreads();
-        // rank every entry among its bin by k (keys are unique within a band
-        // list) and write it to its place in (bin, k) order
-#pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            const int i = tid + u * kTileBlock;
-            if (i >= m_cnt) continue;
-            const uint32_t key = kk[u];
-            const int b0 = s_bstart[bn[u]], b1 = s_bstart[bn[u] + 1];
-            int rank = 0;
-            for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
-            const int q = fdiv((int)key, g.np_div);
-            const float fx = rfx[u], fy = rfy[u], A = ra[u];
-            const float a0 = A * (1.f - fy), a1 = A * fy;
-            s_w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
-            s_row[b0 + rank] = (uint32_t)(q * gq);
-        }
-        if (tid < 3) {
-            s_w[m_cnt + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-            s_row[m_cnt + tid] = 0u;
-        }
-        __syncthreads();
+        stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
         // every group walks its block of bins
-        if (grp_ok) {
-            // terms of four entries of the group's bin (bi, bj): corner (dx, dy)
-            // of such an entry is acc[bi + dy][bj + dx]; the four terms are
-            // summed before they join the pixel's total, which keeps float32
-            // rounding chains short
-            auto add_terms = [&](int bi, int bj, const float4 (&wv)[4], const float (&gv)[4][4]) {
-#pragma unroll
-                for (int dy = 0; dy < 2; ++dy) {
-                    const int pr = bi + dy;
-#pragma unroll
-                    for (int dx = 0; dx < 2; ++dx) {
-                        const int pc = bj + dx;
-                        float4 ts;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const float4 w4 = wv[u];
-                            const float wc = dy ? (dx ? w4.w : w4.z) : (dx ? w4.y : w4.x);
-                            if (u == 0) {
-                                ts = make_float4(wc * gv[u][0], wc * gv[u][1], wc * gv[u][2], wc * gv[u][3]);
-                            } else {
-                                ts.x = __builtin_fmaf(wc, gv[u][0], ts.x);
-                                ts.y = __builtin_fmaf(wc, gv[u][1], ts.y);
-                                ts.z = __builtin_fmaf(wc, gv[u][2], ts.z);
-                                ts.w = __builtin_fmaf(wc, gv[u][3], ts.w);
-                            }
-                        }
-                        acc[pr][pc].x += ts.x;
-                        acc[pr][pc].y += ts.y;
-                        acc[pr][pc].z += ts.z;
-                        acc[pr][pc].w += ts.w;
-                    }
-                }
-            };
-            // entry range [b0, b1) of the group's bin (bi, bj); empty where there is no such bin
-            auto bin_range = [&](int bi, int bj, int& b0, int& b1) {
-                const int by = by0 + bi, bx = bx0 + bj;
-                b0 = b1 = 0;
-                if (by > th || bx > tw) return;
-                const int bin = by * nbw + bx;
-                b0 = s_bstart[bin];
-                b1 = s_bstart[bin + 1];
-            };
-#pragma unroll
-            for (int bi = 0; bi < RH; ++bi) {
-#pragma unroll
-                for (int bj = 0; bj < RW; ++bj) {
-                    int e0, e1;
-                    bin_range(bi, bj, e0, e1);
-                    for (int e = e0; e < e1; e += 4) {
-                        float4 wv[4];
-                        float gv[4][4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            // slots past the bin's end load no row (the buffer
-                            // returns zeros past its end), so whatever
-                            // weights they read add nothing
-                            wv[u] = s_w[e + u];
-                            const uint32_t row = s_row[e + u];
-                            BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
-                        }
-                        add_terms(bi, bj, wv, gv);
-                    }
-                }
-            }
-        }
+        if (grp_ok) walk_bins<T, RH, RW, RH + 1, RW + 1, 1, 1>(s, gr, ch, by0, bx0, th, tw, nbw, acc);
         __syncthreads();
     }
 
-    // halo exchange through LDS (s_w is free now): the halo row goes to the
+    // halo exchange through LDS (s.w is free now): the halo row goes to the
     // group above, the halo column to the group on the left and the corner to
     // the group above-left; a pixel adds its own sum, then the values from
     // below, from the right and from below-right, in that order
     // (a job without entries has nothing to trade)
-    static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s_w");
-    float4* s_x = s_w;
+    static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s.w");
+    float4* s_x = s.w;
     if (run_off[w_hi] > run_off[w_lo]) {
         if (grp_ok) {
 #pragma unroll
@@ -937,8 +1045,6 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // own pixels: band-local (by0 - 1 + i, bx0 - 1 + j) for i, j >= 1
     if (t.nch == 1) {
         // the band's only job: store the final values
-        const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-        T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
 #pragma unroll
         for (int i = 1; i <= RH; ++i)
 #pragma unroll

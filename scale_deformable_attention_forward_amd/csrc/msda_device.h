@@ -88,6 +88,8 @@ constexpr int kRectColsDense = 2;        //   2 columns where samples are dense 
 constexpr int kRectColsSparse = 4;       //   4 where they are sparse (twice the band width: half the jobs)
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
+constexpr int kPixCols = 4;              // pixel mode: a lane group's block is kRectRows x kPixCols pixels
+constexpr int kTileHalo = 0, kTilePixel = 1;  // how a level's bins are walked (TilePlan::mode)
 constexpr int kBandBlock = 512;          // threads of the bucketing kernels
 constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
@@ -115,6 +117,7 @@ struct TilePlan {
     FastDiv rows_div[kMaxLevels];        // by rows[l]
     FastDiv cols_div[kMaxLevels];        // by cols[l]
     int32_t rect_cols;                   // anchor-bin columns per lane group (kRectColsDense / kRectColsSparse)
+    int32_t mode[kMaxLevels];            // kTileHalo or kTilePixel
 };
 
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).

@@ -196,6 +196,15 @@ def test_workspace_size_encoder_shape(lib):
     assert (20 + 8) * samples <= sz.value <= (20 + 16) * samples * 1.5
 
 
+def test_workspace_size_without_samples(lib):
+    # no queries: nothing to bucket or tile, and planning the tiles must not
+    # divide by the sample count
+    for N_q in (0, 1):
+        prob, keep = binding.make_problem(1, 30, N_q, 2, 8, ((5, 6),), (0,), 2)
+        sz = ctypes.c_size_t(123)
+        assert lib.msda_backward_workspace_size(ctypes.byref(prob), ctypes.byref(sz)) == 0
+
+
 def test_bf16_backward_needs_workspace(lib):
     # the generic path (C_h = 6) accumulates bfloat16 grad_value in float32
     prob, keep = _prob(C_h=6, value_dtype=torch.bfloat16)

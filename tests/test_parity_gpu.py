@@ -93,7 +93,7 @@ def test_backward_named_workload_full_size(num, gpu_device):
 def test_backward_decoder_workload_full_size(gpu_device):
     """The decoder workload's shapes (B=8, N_q=300 clustered queries over the
     L=22223 pyramid) with a grad_output: samples are sparse against the
-    pixels, so the tile pass takes its wide-block plan."""
+    pixels, so the tile pass walks the two large levels in pixel mode."""
     d = make_workload(3, grad_seed=1003)
     _check_backward(d, gpu_device, "workload 3 decoder, backward")
 
@@ -264,11 +264,36 @@ def test_many_runs_in_one_pass(gpu_device):
 
 def test_sparse_samples_wide_blocks_and_split_band(gpu_device):
     """16,000 samples per (b, h, level) against 18,000 pixels in the large
-    level: the tile pass takes 2x4-bin blocks per lane group (sparse shape),
-    and the one band of the 6x7 level holds every sample of that level, so it
-    is split into chunks whose partial tiles the reduction adds."""
+    level: the tile pass walks that level in pixel mode, and the 6x7 level
+    (halo mode with 2x4-bin blocks per lane group: the shape is sparse) has
+    one band holding every sample of that level, so it is split into chunks
+    whose partial tiles the reduction adds."""
     d = _mk(levels=((120, 150), (6, 7)), B=1, N_h=2, N_q=4000, C_h=32, N_p=4, seed=31, loc_range=(-0.05, 1.05))
     _check_backward(d, gpu_device, "sparse shape, split band")
+
+
+def test_pixel_mode_band_of_many_passes(gpu_device):
+    """10,000 samples against the 40,000 pixels of a 200x200 level put it in
+    pixel mode, but every location falls in [0, 0.1]^2, so the few bands
+    there hold several LDS passes of entries each: every round of pixel
+    blocks stages its passes again. Matches the oracle, bitwise the same on
+    every run."""
+    d = _mk(levels=((200, 200),), B=1, N_h=2, N_q=2500, C_h=8, N_p=4, seed=37, loc_range=(0.0, 0.1))
+    _check_backward(d, gpu_device, "pixel mode, many passes per band")
+    runs = [_gpu_backward(d, gpu_device, (True, False, False))[0] for _ in range(2)]
+    np.testing.assert_array_equal(runs[0], runs[1])
+
+
+def test_pixel_mode_repeat_runs_are_stable(gpu_device):
+    """Decoder-like sparse samples (pixel mode on the two large levels):
+    grad_value is bitwise the same on every run."""
+    d = _mk(levels=((60, 80), (30, 40), (8, 10)), B=2, N_h=4, N_q=200, C_h=32, N_p=4, seed=41,
+            loc_range=(-0.05, 1.05))
+    runs = [_gpu_backward(d, gpu_device, (True, False, False))[0] for _ in range(3)]
+    for r in runs[1:]:
+        np.testing.assert_array_equal(runs[0], r)
+    compare("pixel mode repeat", runs[0], oracle_backward(d, compute_grad_sampling_locations=False,
+                                                          compute_grad_attention_weights=False)[0], RTOL["fp32"])
 
 
 def test_autograd_function_matches_oracle(gpu_device):
