@@ -209,23 +209,23 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
     const int64_t nsamp = p.N_q * p.N_p;
     const int64_t nwg = std::max<int64_t>(1, (nsamp + msda::kBandChunk - 1) / msda::kBandChunk);
     if (nwg >= 65536) return false;  // grid x of the bucketing kernels stays small
-    int64_t jobs = 0, bands = 0, cap = 0, part = 0, pieces = 0;
+    int64_t jobs = 0, pjobs = 0, bands = 0, cap = 0, part = 0, pieces = 0;
     for (int64_t l = 0; l < msda::kMaxLevels; ++l) {
         tp->job_begin[l] = (int32_t)jobs;
+        tp->pjob_begin[l] = (int32_t)pjobs;
         tp->band_begin[l] = (int32_t)bands;
         tp->part_off[l] = (int32_t)part;
         tp->rpiece_begin[l] = (int32_t)pieces;
         tp->rpieces_per_band[l] = 1;
         tp->rows_div[l] = msda::make_fastdiv(1);
         tp->cols_div[l] = msda::make_fastdiv(1);
-        tp->mode[l] = msda::kTileHalo;
         if (l >= p.N_l) {
             tp->rows[l] = tp->row_bands[l] = tp->cols[l] = tp->col_bands[l] = tp->chunks[l] = 1;
             continue;
         }
         const int64_t H = p.spatial_shapes[2 * l], W = p.spatial_shapes[2 * l + 1];
         int64_t rows = 0, cols = 0, rb = 0, cb = 0;
-        tp->mode[l] = msda::kTileHalo;
+        bool pixel = false;
         if (nsamp > 0 && nsamp < H * W) {
             // pixel mode: bands of at most kTileBins anchor bins holding about
             // three quarters of a pass of entries if locations spread evenly
@@ -244,11 +244,11 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
                     cb = ncb;
                 }
             }
-            if (rows > 0) tp->mode[l] = msda::kTilePixel;
+            pixel = rows > 0;
         }
         // halo mode: a band of r x c pixels has (r + 1) x (c + 1) anchor bins,
         // dealt out to ny x nx lane groups in blocks of RH x RW bins
-        const int64_t nx_max = tp->mode[l] == msda::kTilePixel ? 0 : std::min<int64_t>(groups, W / RW + 1);
+        const int64_t nx_max = pixel ? 0 : std::min<int64_t>(groups, W / RW + 1);
         for (int64_t nx = 1; nx <= nx_max; ++nx) {
             const int64_t ny = std::min<int64_t>(groups / nx, H / RH + 1);
             const int64_t r = std::min<int64_t>(H, ny * RH - 1), c = std::min<int64_t>(W, nx * RW - 1);
@@ -267,7 +267,7 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         const int64_t expect = nsamp * (rows + 1) / (H + 1) * (cols + 1) / (W + 1) + 1;
         int64_t chunks = (expect + 3 * msda::kTileEntries - 1) / (3 * msda::kTileEntries);
         chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, std::min<int64_t>(nwg, 1024)));  // >= 1 run each
-        if (tp->mode[l] == msda::kTilePixel) chunks = 1;  // pixel-mode bands are not split
+        if (pixel) chunks = 1;  // pixel-mode bands are not split
         tp->rows[l] = (int32_t)rows;
         tp->rows_div[l] = msda::make_fastdiv((uint32_t)rows);
         tp->cols_div[l] = msda::make_fastdiv((uint32_t)cols);
@@ -275,7 +275,7 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         tp->cols[l] = (int32_t)cols;
         tp->col_bands[l] = (int32_t)cb;
         tp->chunks[l] = (int32_t)chunks;
-        jobs += rb * cb * chunks;
+        (pixel ? pjobs : jobs) += rb * cb * chunks;
         bands += rb * cb;
         cap += nsamp * (cb > 1 ? 4 : 2);  // a sample touches at most 2 row bands x 2 column bands
         if (chunks > 1) {
@@ -288,14 +288,16 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         if (part >= kIndexLimit || pieces >= kIndexLimit) return false;
     }
     tp->job_begin[msda::kMaxLevels] = (int32_t)jobs;
+    tp->pjob_begin[msda::kMaxLevels] = (int32_t)pjobs;
     tp->rpiece_begin[msda::kMaxLevels] = (int32_t)pieces;
     tp->jobs = (int32_t)jobs;
+    tp->pjobs = (int32_t)pjobs;
     tp->bands = (int32_t)bands;
     tp->rpieces = (int32_t)pieces;
     tp->nwg = (int32_t)nwg;
     tp->cap = cap;
     tp->part_per_slab = part;
-    return jobs < kIndexLimit && cap < kIndexLimit && bands * nwg + 1 < kIndexLimit &&
+    return jobs < kIndexLimit && pjobs < kIndexLimit && cap < kIndexLimit && bands * nwg + 1 < kIndexLimit &&
            (int64_t)p.B * p.N_h * (bands * nwg + 1) < kIndexLimit;
 }
 
@@ -459,7 +461,7 @@ msda_status backward_call(const msda_problem* problem, const void* grad_output, 
     g.units = (int32_t)units;
     g.blocks = (int32_t)((units + upb - 1) / upb);
     g.loc_pair_aligned = aligned(sampling_locations, 8) && (!grad_sampling_locations || aligned(grad_sampling_locations, 8));
-    if (fast && grad_value && !empty && (int64_t)tp.jobs * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
+    if (fast && grad_value && !empty && (int64_t)(tp.jobs + tp.pjobs) * g.B * g.Nh >= kIndexLimit) return MSDA_ERR_UNSUPPORTED;
     if (need_out) return MSDA_OK;
 
     hipError_t e = hipSuccess;

@@ -416,7 +416,7 @@ struct BandWs {
 };
 
 struct LevelTiles {
-    int H, W, start, R, CW, nbr, nbc, nch, band0, job0, part, mode;
+    int H, W, start, R, CW, nbr, nbc, nch, band0, job0, pjob0, part;
     FastDiv rd, cd;  // by R, by CW
 };
 
@@ -437,8 +437,8 @@ __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TileP
             t.nch = tp.chunks[k];
             t.band0 = tp.band_begin[k];
             t.job0 = tp.job_begin[k];
+            t.pjob0 = tp.pjob_begin[k];
             t.part = tp.part_off[k];
-            t.mode = tp.mode[k];
             t.rd = tp.rows_div[k];
             t.cd = tp.cols_div[k];
         }
@@ -645,8 +645,8 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 //    thus loaded once and applied to all four corners; after the passes the
 //    groups hand their halos to their neighbours through LDS, which add
 //    them in a fixed order;
-//  - pixel mode (levels with fewer samples than pixels): bands are as large
-//    as the bin table allows and every group owns blocks of kRectRows x
+//  - pixel mode (levels with fewer samples than pixels; tile_pixel_kernel):
+//    bands are as large as the bin table allows and every group owns blocks of kRectRows x
 //    kPixCols pixels, one block per round, walking the (kRectRows + 1) x
 //    (kPixCols + 1) bins around it and keeping only the corners that fall in
 //    its block. An entry's row is loaded by every group it reaches (up to
@@ -876,6 +876,10 @@ __device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc
     }
 }
 
+// Halo-mode tile kernel. It keeps its own copy of the staging and the walk
+// (the same results as stage_pass and walk_bins; its bin scan goes 512 bins
+// at a time): built from those shared functions it took 1-2% longer (more
+// scalar registers spilled).
 template <typename T, int LPU, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
@@ -883,7 +887,16 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
 {
     constexpr int RH = kRectRows;
     constexpr int E = kTileEntries;
-    __shared__ TileLds s;
+    constexpr int kWaves = kTileBlock / kWave;
+    // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
+    // A fy (1-fx), A fy fx and the element offset q * N_h * C_h of the
+    // grad_output row; the three slots after a pass's last entry hold zeros
+    __shared__ float4 s_w[E + 3];
+    __shared__ uint32_t s_row[E + 3];
+    __shared__ uint32_t s_bkey[E];           // sample indices k in binned order
+    __shared__ int s_bstart[kTileBins + 1];  // bin boundaries in s_w / s_row
+    __shared__ int s_cursor[kTileBins];
+    __shared__ int s_wave[kWaves];
 
     const int tid = threadIdx.x;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -908,63 +921,15 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // this chunk's runs [w_lo, w_hi) of the band's list; run_off[w] is where run w starts
     const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
     const int w_lo = (int)((int64_t)tp.nwg * chunk / t.nch), w_hi = (int)((int64_t)tp.nwg * (chunk + 1) / t.nch);
-    const uint32_t* list = w.k + (size_t)slab * tp.cap;
+    const size_t lbase = (size_t)slab * tp.cap;
     const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
     const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
     const int gq = g.Nh * g.Ch;
     // rows of this slab: q * gq elements past grow0, as byte offsets of a buffer over the slab's span
     const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, (int64_t)g.Nq * gq * (int64_t)sizeof(T));
-    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
-    T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;  // + pixel * pstride
 
     const int grp = tid / LPU, lig = tid % LPU;
     const int ch = lig * 4;
-
-    if (t.mode == kTilePixel) {
-        // ---- pixel mode: rounds of kRectRows x kPixCols pixel blocks ----
-        constexpr int PC = kPixCols;
-        constexpr int kGroups = kTileBlock / LPU;
-        const int pbw = (tw + PC - 1) / PC, nblk = ((th + RH - 1) / RH) * pbw;
-        int wn, p0, m_cnt;
-        find_pass(run_off, w_lo, w_hi, wn, p0, m_cnt);
-        const bool single = wn >= w_hi;  // one pass: staged once for every round
-        if (single) stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
-        for (int rb = 0; rb < nblk; rb += kGroups) {
-            const int blk = rb + grp;
-            const bool own = blk < nblk && ch < g.Ch;
-            const int pby = own ? blk / pbw : 0, pbx = own ? blk - (blk / pbw) * pbw : 0;
-            const int py0 = pby * RH, px0 = pbx * PC;  // the block's first pixel, band-local
-            float4 acc[RH][PC];
-#pragma unroll
-            for (int i = 0; i < RH; ++i)
-#pragma unroll
-                for (int j = 0; j < PC; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int wr = w_lo; wr < w_hi;) {
-                if (!single) {
-                    find_pass(run_off, wr, w_hi, wn, p0, m_cnt);
-                    stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
-                }
-                // bins py0..py0+RH, px0..px0+PC reach the block (bin (by, bx)
-                // is anchored at band-local pixel (by - 1, bx - 1))
-                if (own) walk_bins<T, RH + 1, PC + 1, RH, PC, 0, 0>(s, gr, ch, py0, px0, th, tw, nbw, acc);
-                if (!single) __syncthreads();  // the next pass is staged over this one
-                wr = wn;
-            }
-            if (own) {
-#pragma unroll
-                for (int i = 0; i < RH; ++i)
-#pragma unroll
-                    for (int j = 0; j < PC; ++j) {
-                        const int py = py0 + i, px = px0 + j;
-                        if (py < th && px < tw)
-                            store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[i][j], accumulate);
-                    }
-            }
-        }
-        return;
-    }
-
-    // ---- halo mode ----
     const int gnx = (tw + RW) / RW, gny = (th + RH) / RH;  // group blocks cover the (th+1) x (tw+1) bins
     const int gy = grp / gnx, gx = grp - gy * gnx;
     const int by0 = gy * RH, bx0 = gx * RW;  // the group's first bin (bin row 0 is anchor row r0 - 1)
@@ -983,22 +948,185 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // order inside runs; inside a pass every bin is summed in k order. The
     // sums are therefore the same on every call.
     for (int wr = w_lo; wr < w_hi;) {
-        int wn, p0, m_cnt;
-        find_pass(run_off, wr, w_hi, wn, p0, m_cnt);
+        const int p0 = run_off[wr];
+        // the pass ends before the first run that would overflow E entries;
+        // run ends never decrease, so the lanes test 64 runs per load instead
+        // of walking them one dependent load at a time
+        int wn = wr + 1;
+        while (wn < w_hi) {
+            const int w = wn + tid % kWave;
+            const uint64_t fits = __ballot(w < w_hi && run_off[w + 1] - p0 <= E);
+            if (~fits == 0) {
+                wn += kWave;
+                continue;
+            }
+            wn += __ffsll((unsigned long long)~fits) - 1;
+            break;
+        }
+        const int m_cnt = run_off[wn] - p0;
         wr = wn;
-        stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
+        // stage a pass of list entries and count them per anchor bin
+        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
+        __syncthreads();
+        // (each thread keeps its entries' sample indices, bins and records in
+        // registers until it writes them to LDS in their sorted place)
+        constexpr int kStage = kTileEntries / kTileBlock;
+        uint32_t kk[kStage];
+        int bn[kStage];
+        float rfx[kStage], rfy[kStage], ra[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            kk[u] = i < m_cnt ? __builtin_nontemporal_load(w.k + lbase + p0 + i) : 0u;  // read once
+        }
+        // each entry's record (anchor corner, fractions, attention weight) as
+        // the backward kernel wrote it (read about once)
+        f32x4_t rc[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            rc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (tid + u * kTileBlock < m_cnt)
+                rc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(srec + kk[u]));
+        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            if (i >= m_cnt) continue;
+            int x0, y0;
+            unpack_anchor(__float_as_uint(rc[u].x), x0, y0);
+            rfx[u] = rc[u].y;
+            rfy[u] = rc[u].z;
+            ra[u] = rc[u].w;
+            bn[u] = (y0 - r0 + 1) * nbw + (x0 - c0 + 1);
+            atomicAdd(&s_cursor[bn[u]], 1);
+        }
+        __syncthreads();
+        // exclusive scan of the bin counts
+        for (int base = 0; base < nbins; base += kTileBlock) {
+            const int i = base + tid;
+            const int v = i < nbins ? s_cursor[i] : 0;
+            int incl = v;
+            const int lane = tid % kWave, wave = tid / kWave;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int u = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += u;
+            }
+            if (lane == kWave - 1) s_wave[wave] = incl;
+            __syncthreads();
+            int before = base == 0 ? 0 : s_bstart[base];
+            for (int ww = 0; ww < wave; ++ww) before += s_wave[ww];
+            if (i < nbins) s_bstart[i] = before + incl - v;
+            if (tid == kTileBlock - 1) {
+                int tot = base == 0 ? 0 : s_bstart[base];
+                for (int ww = 0; ww < kWaves; ++ww) tot += s_wave[ww];
+                s_bstart[min(base + kTileBlock, nbins)] = tot;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kStage; ++u)
+            if (tid + u * kTileBlock < m_cnt) s_bkey[atomicAdd(&s_cursor[bn[u]], 1)] = kk[u];
+        __syncthreads();
+        // rank every entry among its bin by k (keys are unique within a band
+        // list) and write it to its place in (bin, k) order
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = tid + u * kTileBlock;
+            if (i >= m_cnt) continue;
+            const uint32_t key = kk[u];
+            const int b0 = s_bstart[bn[u]], b1 = s_bstart[bn[u] + 1];
+            int rank = 0;
+            for (int j = b0; j < b1; ++j) rank += s_bkey[j] < key ? 1 : 0;
+            const int q = fdiv((int)key, g.np_div);
+            const float fx = rfx[u], fy = rfy[u], A = ra[u];
+            const float a0 = A * (1.f - fy), a1 = A * fy;
+            s_w[b0 + rank] = make_float4(a0 * (1.f - fx), a0 * fx, a1 * (1.f - fx), a1 * fx);
+            s_row[b0 + rank] = (uint32_t)(q * gq);
+        }
+        if (tid < 3) {
+            s_w[m_cnt + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+            s_row[m_cnt + tid] = 0u;
+        }
+        __syncthreads();
         // every group walks its block of bins
-        if (grp_ok) walk_bins<T, RH, RW, RH + 1, RW + 1, 1, 1>(s, gr, ch, by0, bx0, th, tw, nbw, acc);
+        if (grp_ok) {
+            // terms of four entries of the group's bin (bi, bj): corner (dx, dy)
+            // of such an entry is acc[bi + dy][bj + dx]; the four terms are
+            // summed before they join the pixel's total, which keeps float32
+            // rounding chains short
+            auto add_terms = [&](int bi, int bj, const float4 (&wv)[4], const float (&gv)[4][4]) {
+#pragma unroll
+                for (int dy = 0; dy < 2; ++dy) {
+                    const int pr = bi + dy;
+#pragma unroll
+                    for (int dx = 0; dx < 2; ++dx) {
+                        const int pc = bj + dx;
+                        float4 ts;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float4 w4 = wv[u];
+                            const float wc = dy ? (dx ? w4.w : w4.z) : (dx ? w4.y : w4.x);
+                            if (u == 0) {
+                                ts = make_float4(wc * gv[u][0], wc * gv[u][1], wc * gv[u][2], wc * gv[u][3]);
+                            } else {
+                                ts.x = __builtin_fmaf(wc, gv[u][0], ts.x);
+                                ts.y = __builtin_fmaf(wc, gv[u][1], ts.y);
+                                ts.z = __builtin_fmaf(wc, gv[u][2], ts.z);
+                                ts.w = __builtin_fmaf(wc, gv[u][3], ts.w);
+                            }
+                        }
+                        acc[pr][pc].x += ts.x;
+                        acc[pr][pc].y += ts.y;
+                        acc[pr][pc].z += ts.z;
+                        acc[pr][pc].w += ts.w;
+                    }
+                }
+            };
+            // entry range [b0, b1) of the group's bin (bi, bj); empty where there is no such bin
+            auto bin_range = [&](int bi, int bj, int& b0, int& b1) {
+                const int by = by0 + bi, bx = bx0 + bj;
+                b0 = b1 = 0;
+                if (by > th || bx > tw) return;
+                const int bin = by * nbw + bx;
+                b0 = s_bstart[bin];
+                b1 = s_bstart[bin + 1];
+            };
+#pragma unroll
+            for (int bi = 0; bi < RH; ++bi) {
+#pragma unroll
+                for (int bj = 0; bj < RW; ++bj) {
+                    int e0, e1;
+                    bin_range(bi, bj, e0, e1);
+                    for (int e = e0; e < e1; e += 4) {
+                        float4 wv[4];
+                        float gv[4][4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            // slots past the bin's end load no row (the buffer
+                            // returns zeros past its end), so whatever
+                            // weights they read add nothing
+                            wv[u] = s_w[e + u];
+                            const uint32_t row = s_row[e + u];
+                            BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
+                        }
+                        add_terms(bi, bj, wv, gv);
+                    }
+                }
+            }
+        }
         __syncthreads();
     }
 
-    // halo exchange through LDS (s.w is free now): the halo row goes to the
+    // halo exchange through LDS (s_w is free now): the halo row goes to the
     // group above, the halo column to the group on the left and the corner to
     // the group above-left; a pixel adds its own sum, then the values from
     // below, from the right and from below-right, in that order
     // (a job without entries has nothing to trade)
-    static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s.w");
-    float4* s_x = s.w;
+    static_assert(RW * kTileBlock <= E + 3 && (RH + 1) * kTileBlock <= E + 3, "halo exchange fits s_w");
+    float4* s_x = s_w;
     if (run_off[w_hi] > run_off[w_lo]) {
         if (grp_ok) {
 #pragma unroll
@@ -1045,6 +1173,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
     // own pixels: band-local (by0 - 1 + i, bx0 - 1 + j) for i, j >= 1
     if (t.nch == 1) {
         // the band's only job: store the final values
+        const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+        T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;
 #pragma unroll
         for (int i = 1; i <= RH; ++i)
 #pragma unroll
@@ -1069,6 +1199,86 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             if (py < th && px < tw)
                 nt_store4(slot + (py * tw + px) * g.Ch + ch, acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w);
         }
+}
+
+// Pixel-mode tile kernel (levels with fewer samples than pixels): one
+// workgroup per band; the lane groups take the band's kRectRows x kPixCols
+// pixel blocks in rounds, each walking the bins around its block.
+template <typename T, int LPU>
+__global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_pixel_kernel(
+    Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value, int accumulate)
+{
+    constexpr int RH = kRectRows;
+    __shared__ TileLds s;
+
+    const int tid = threadIdx.x;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int slab = lb / tp.pjobs;
+    const int job = tp.pjobs - 1 - (lb - slab * tp.pjobs);  // coarser levels first, as in halo mode
+    const int b = slab / g.Nh, h = slab - b * g.Nh;
+
+    int l = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k)
+        if (job >= tp.pjob_begin[k] && job < tp.pjob_begin[k + 1]) l = k;
+    const LevelTiles t = level_tiles(g, tp, l);
+    const int band = job - t.pjob0;  // pixel-mode bands are not split
+    const BandRect br = band_rect(t, band);
+    const int r0 = br.r0, c0 = br.c0, tw = br.tw, th = br.th;
+    const int nbw = tw + 1;  // anchor bins cover rows r0-1..r1-1, cols c0-1..c1-1
+    const int nbins = (th + 1) * nbw;
+    // the band's runs [0, nwg); run_off[w] is where run w starts
+    const int* run_off = w.off + (size_t)slab * (tp.bands * tp.nwg + 1) + (size_t)(t.band0 + band) * tp.nwg;
+    const int w_lo = 0, w_hi = tp.nwg;
+    const uint32_t* list = w.k + (size_t)slab * tp.cap;
+    const float4* srec = w.rec + (size_t)(slab * g.Nl + l) * (g.Nq * g.Np);  // records of this (slab, level)
+    const T* grow0 = grad_out + (b * g.Nq * g.Nh + h) * g.Ch;  // + q * N_h * C_h
+    const int gq = g.Nh * g.Ch;
+    const __amdgpu_buffer_rsrc_t gr = value_rsrc(grow0, (int64_t)g.Nq * gq * (int64_t)sizeof(T));
+    const int pstride = g.bnlc ? g.Ch : g.Nh * g.Ch;
+    T* out = grad_value + value_slab_offset(g, b, h) + t.start * pstride;  // + pixel * pstride
+    const int grp = tid / LPU, lig = tid % LPU;
+    const int ch = lig * 4;
+
+    constexpr int PC = kPixCols;
+    constexpr int kGroups = kTileBlock / LPU;
+    const int pbw = (tw + PC - 1) / PC, nblk = ((th + RH - 1) / RH) * pbw;
+    int wn, p0, m_cnt;
+    find_pass(run_off, w_lo, w_hi, wn, p0, m_cnt);
+    const bool single = wn >= w_hi;  // one pass: staged once for every round
+    if (single) stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
+    for (int rb = 0; rb < nblk; rb += kGroups) {
+        const int blk = rb + grp;
+        const bool own = blk < nblk && ch < g.Ch;
+        const int pby = own ? blk / pbw : 0, pbx = own ? blk - (blk / pbw) * pbw : 0;
+        const int py0 = pby * RH, px0 = pbx * PC;  // the block's first pixel, band-local
+        float4 acc[RH][PC];
+#pragma unroll
+        for (int i = 0; i < RH; ++i)
+#pragma unroll
+            for (int j = 0; j < PC; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int wr = w_lo; wr < w_hi;) {
+            if (!single) {
+                find_pass(run_off, wr, w_hi, wn, p0, m_cnt);
+                stage_pass(s, g, list, srec, p0, m_cnt, r0, c0, nbw, nbins, gq);
+            }
+            // bins py0..py0+RH, px0..px0+PC reach the block (bin (by, bx)
+            // is anchored at band-local pixel (by - 1, bx - 1))
+            if (own) walk_bins<T, RH + 1, PC + 1, RH, PC, 0, 0>(s, gr, ch, py0, px0, th, tw, nbw, acc);
+            if (!single) __syncthreads();  // the next pass is staged over this one
+            wr = wn;
+        }
+        if (own) {
+#pragma unroll
+            for (int i = 0; i < RH; ++i)
+#pragma unroll
+                for (int j = 0; j < PC; ++j) {
+                    const int py = py0 + i, px = px0 + j;
+                    if (py < th && px < tw)
+                        store_grad4(out + ((r0 + py) * t.W + c0 + px) * pstride + ch, acc[i][j], accumulate);
+                }
+        }
+    }
 }
 
 // Adds the partial tiles of split bands in chunk order and stores grad_value.
@@ -1283,8 +1493,14 @@ static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, 
     // batch span fewer than 2^31 - 2^20 bytes (tile_rows_fit), so the walk's
     // buffer loads reach every row
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
-    hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream, g,
-                       tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial, accumulate);
+    if (blocks > 0)
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
+                           g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial,
+                           accumulate);
+    const int64_t pblocks = (int64_t)tp.pjobs * g.B * g.Nh;
+    if (pblocks > 0)
+        hipLaunchKernelGGL((tile_pixel_kernel<T, LPU>), dim3((unsigned)pblocks), dim3(kTileBlock), 0, stream, g, tp,
+                           w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), accumulate);
 }
 
 template <typename T, int LPU>

@@ -89,7 +89,6 @@ constexpr int kRectColsSparse = 4;       //   4 where they are sparse (twice the
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
 constexpr int kPixCols = 4;              // pixel mode: a lane group's block is kRectRows x kPixCols pixels
-constexpr int kTileHalo = 0, kTilePixel = 1;  // how a level's bins are walked (TilePlan::mode)
 constexpr int kBandBlock = 512;          // threads of the bucketing kernels
 constexpr int kBandChunk = 2048;         // samples per bucketing workgroup
 constexpr int kMaxBandsPerLevel = 4096;  // bands of one level (LDS histogram size)
@@ -98,7 +97,8 @@ static_assert(kBandChunk <= kTileEntries, "one run (<= kBandChunk entries) must 
 static_assert(kBandChunk % kBandBlock == 0 && kTileEntries % kTileBlock == 0, "whole per-thread batches");
 
 struct TilePlan {
-    int32_t jobs;                        // tile jobs per (b, h) slab
+    int32_t jobs;                        // halo-mode tile jobs per (b, h) slab
+    int32_t pjobs;                       // pixel-mode tile jobs (bands) per (b, h) slab
     int32_t bands;                       // bands per slab
     int32_t rpieces;                     // reduction pieces per slab (0: no band is split)
     int32_t nwg;                         // bucketing workgroups (runs) per (slab, level)
@@ -110,14 +110,14 @@ struct TilePlan {
     int32_t col_bands[kMaxLevels];
     int32_t chunks[kMaxLevels];
     int32_t band_begin[kMaxLevels];      // first band of level l within the slab
-    int32_t job_begin[kMaxLevels + 1];
+    int32_t job_begin[kMaxLevels + 1];   // first halo-mode job of level l (none for pixel-mode levels)
+    int32_t pjob_begin[kMaxLevels + 1];  // first pixel-mode job of level l (none for halo-mode levels)
     int32_t part_off[kMaxLevels];        // first partial-tile float of level l within the slab
     int32_t rpieces_per_band[kMaxLevels];
     int32_t rpiece_begin[kMaxLevels + 1];
     FastDiv rows_div[kMaxLevels];        // by rows[l]
     FastDiv cols_div[kMaxLevels];        // by cols[l]
     int32_t rect_cols;                   // anchor-bin columns per lane group (kRectColsDense / kRectColsSparse)
-    int32_t mode[kMaxLevels];            // kTileHalo or kTilePixel
 };
 
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).
