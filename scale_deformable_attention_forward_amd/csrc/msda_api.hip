@@ -39,6 +39,7 @@ using msda::Geometry;
 using msda::TilePlan;
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // kernels index with 32-bit offsets
+constexpr int64_t kForwardMinWaves = 8192;           // about 8 waves per SIMD of the 1,024 (256 CUs x 4)
 
 struct Sizes {
     int64_t value_elems, loc_elems, attn_elems, out_elems;
@@ -536,11 +537,17 @@ msda_status msda_forward(const msda_problem* problem, const void* value, const f
         overlap(output, z.out_bytes, attention_weights, attn_bytes))
         return MSDA_ERR_INVALID_ARGUMENT;
 
-    const int vec = pick_vec(problem->C_h, z.elem, {value, output});
-    const int lanes = (int)std::min<int64_t>(64, (problem->C_h + vec - 1) / vec);
-    g.lpu_log2 = ilog2(lanes);
-    const int64_t per_chunk = ((int64_t)1 << g.lpu_log2) * vec;
-    g.chunks = (int32_t)((problem->C_h + per_chunk - 1) / per_chunk);
+    // Widest vector the alignment allows; for small problems narrower ones,
+    // which spread a unit's channels over more lanes (each channel's
+    // multiply-add chain, and so every output bit, stays the same), until
+    // the grid has kForwardMinWaves waves to cover the gathers' latency.
+    int vec = pick_vec(problem->C_h, z.elem, {value, output});
+    auto lanes_for = [&](int v) { return 1 << ilog2((int)std::min<int64_t>(64, (problem->C_h + v - 1) / v)); };
+    auto chunks_for = [&](int v) { return (problem->C_h + (int64_t)lanes_for(v) * v - 1) / ((int64_t)lanes_for(v) * v); };
+    auto waves_for = [&](int v) { return (int64_t)g.B * g.Nh * g.Nq * chunks_for(v) * lanes_for(v) / msda::kWave; };
+    while (vec > 1 && waves_for(vec) < kForwardMinWaves) vec /= 2;
+    g.lpu_log2 = ilog2(lanes_for(vec));
+    g.chunks = (int32_t)chunks_for(vec);
     g.ch_div = msda::make_fastdiv((uint32_t)g.chunks);
     const int64_t units = (int64_t)g.B * g.Nh * g.Nq * g.chunks;
     const int64_t upb = msda::kBlock >> g.lpu_log2;
