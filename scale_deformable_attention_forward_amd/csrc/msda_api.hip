@@ -179,7 +179,8 @@ bool fast_backward_shape(const msda_problem& p)
 // Levels with fewer samples per slab than pixels take pixel mode: bands of
 // at most kTileBins anchor bins expected to hold about three quarters of
 // one LDS pass of entries, fewest bands first, walked by lane groups that
-// own pixel blocks. Every other level takes halo mode: the
+// own pixel blocks; so do levels small enough for one such band. Every
+// other level takes halo mode: the
 // (rows + 1) x (cols + 1) anchor bins of a band are dealt out to ny x nx lane
 // groups in blocks of kRectRows x RW bins (ny * nx <= the groups of one tile
 // workgroup), so rows = ny * kRectRows - 1 and cols = nx * RW - 1 (or the
@@ -230,22 +231,35 @@ bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
         if (nsamp > 0 && nsamp < H * W) {
             // pixel mode: bands of at most kTileBins anchor bins holding about
             // three quarters of a pass of entries if locations spread evenly
-            // (so one pass is the rule), fewest bands, then fewest column bands
+            // (so one pass is the rule), fewest bands, then fewest column
+            // bands. Only the smallest band height giving each row-band
+            // count can win (a taller band only narrows the columns), so
+            // the heights tried are the distinct values of ceil(H / k).
             const int64_t r_max = std::min<int64_t>(H, msda::kTileBins / 2 - 1);
-            for (int64_t r = 1; r <= r_max; ++r) {
-                const int64_t c_bins = msda::kTileBins / (r + 1) - 1;
-                const int64_t c_fill = 3 * msda::kTileEntries / 4 * (H + 1) * (W + 1) / (nsamp * (r + 1)) - 1;
-                const int64_t c = std::min<int64_t>(W, std::min(c_bins, c_fill));
-                if (c < 1) continue;
-                const int64_t nrb = (H + r - 1) / r, ncb = (W + c - 1) / c;
-                if (rows == 0 || nrb * ncb < rb * cb || (nrb * ncb == rb * cb && ncb < cb)) {
-                    rows = r;
-                    cols = c;
-                    rb = nrb;
-                    cb = ncb;
+            for (int64_t k = 1; k <= H;) {
+                const int64_t r = (H + k - 1) / k;  // the smallest height with ceil(H / r) row bands
+                if (r <= r_max) {
+                    const int64_t c_bins = msda::kTileBins / (r + 1) - 1;
+                    const int64_t c_fill = 3 * msda::kTileEntries / 4 * (H + 1) * (W + 1) / (nsamp * (r + 1)) - 1;
+                    const int64_t c = std::min<int64_t>(W, std::min(c_bins, c_fill));
+                    const int64_t nrb = (H + r - 1) / r, ncb = c >= 1 ? (W + c - 1) / c : 0;
+                    if (c >= 1 && (rows == 0 || nrb * ncb < rb * cb || (nrb * ncb == rb * cb && ncb < cb))) {
+                        rows = r;
+                        cols = c;
+                        rb = nrb;
+                        cb = ncb;
+                    }
                 }
+                if (r == 1) break;
+                k = (H + r - 2) / (r - 1);  // the first k with a smaller height
             }
             pixel = rows > 0;
+        } else if (nsamp > 0 && (H + 1) * (W + 1) <= msda::kTileBins && nsamp <= 3 * msda::kTileEntries / 4) {
+            // a small level that one pixel-mode band covers with about one pass
+            rows = H;
+            cols = W;
+            rb = cb = 1;
+            pixel = true;
         }
         // halo mode: a band of r x c pixels has (r + 1) x (c + 1) anchor bins,
         // dealt out to ny x nx lane groups in blocks of RH x RW bins
