@@ -25,7 +25,7 @@ def _say(msg):
 
 @pytest.mark.parametrize("dtype,C_h,levels,N_q", [
     ("fp32", 32, ((20, 30), (10, 15), (5, 8)), 500),   # halo-mode tile pass
-    ("fp32", 32, ((60, 80), (8, 10)), 100),             # pixel mode on the large level
+    ("fp32", 32, ((60, 80), (8, 10)), 100),             # pixel mode (both levels)
     ("bf16", 32, ((20, 30), (10, 15)), 400),
     ("fp32", 6, ((12, 16), (6, 8)), 50),                # generic path (float atomics)
 ])

@@ -285,7 +285,8 @@ def test_pixel_mode_band_of_many_passes(gpu_device):
 
 
 def test_pixel_mode_repeat_runs_are_stable(gpu_device):
-    """Decoder-like sparse samples (pixel mode on the two large levels):
+    """Decoder-like sparse samples (pixel mode on every level: the two large
+    ones have fewer samples than pixels, one band covers the small one):
     grad_value is bitwise the same on every run."""
     d = _mk(levels=((60, 80), (30, 40), (8, 10)), B=2, N_h=4, N_q=200, C_h=32, N_p=4, seed=41,
             loc_range=(-0.05, 1.05))
