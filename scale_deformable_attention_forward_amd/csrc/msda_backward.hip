@@ -802,23 +802,23 @@ __device__ __forceinline__ void stage_pass(TileLds& s, const Geometry& g, const 
     __syncthreads();
 }
 
-// Terms of four entries of one bin for the pixels of a group's accumulator
-// window: corner (dx, dy) of an entry in window bin (bi, bj) is window
-// pixel (bi - 1 + dy + OY, bj - 1 + dx + OX) (OY = OX = 1 in halo mode,
-// where window row and column 0 are the halo; 0 in pixel mode); corners
-// outside the window are dropped. The four entries' terms are summed before
-// they join the pixel's total, which keeps float32 rounding chains short.
-template <int WR, int WC, int OY, int OX>
+// Pixel mode: terms of four entries of window bin (bi, bj) for a lane
+// group's block of WR x WC pixels; the bin is anchored at block pixel
+// (bi - 1, bj - 1), so corner (dx, dy) of an entry lands on block pixel
+// (bi - 1 + dy, bj - 1 + dx), and corners outside the block are dropped. The
+// four entries' terms are summed before they join the pixel's total, which
+// keeps float32 rounding chains short.
+template <int WR, int WC>
 __device__ __forceinline__ void add_bin_terms(float4 (&acc)[WR][WC], int bi, int bj, const float4 (&wv)[4],
                                               const float (&gv)[4][4])
 {
 #pragma unroll
     for (int dy = 0; dy < 2; ++dy) {
-        const int pr = bi - 1 + dy + OY;
+        const int pr = bi - 1 + dy;
         if (pr < 0 || pr >= WR) continue;
 #pragma unroll
         for (int dx = 0; dx < 2; ++dx) {
-            const int pc = bj - 1 + dx + OX;
+            const int pc = bj - 1 + dx;
             if (pc < 0 || pc >= WC) continue;
             float4 ts;
 #pragma unroll
@@ -842,20 +842,20 @@ __device__ __forceinline__ void add_bin_terms(float4 (&acc)[WR][WC], int bi, int
     }
 }
 
-// Walk bins (by0 + bi, bx0 + bj), bi < BR, bj < BC, of the staged pass
-// (bins past the band's th x tw pixels are empty), four entries at a time:
-// their grad_output rows are loaded (slots past a bin's end load no row: the
-// buffer returns zeros past its end, so whatever weights they read add
-// nothing) and their terms added to the window.
-template <typename T, int BR, int BC, int WR, int WC, int OY, int OX>
-__device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc_t gr, int ch, int by0, int bx0,
+// Pixel mode: walk the (WR + 1) x (WC + 1) bins around the block whose first
+// pixel is (py0, px0) (bins past the band's th x tw pixels are empty), four
+// entries at a time: their grad_output rows are loaded (slots past a bin's
+// end load no row: the buffer returns zeros past its end, so whatever weights
+// they read add nothing) and their terms added to the block.
+template <typename T, int WR, int WC>
+__device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc_t gr, int ch, int py0, int px0,
                                           int th, int tw, int nbw, float4 (&acc)[WR][WC])
 {
 #pragma unroll
-    for (int bi = 0; bi < BR; ++bi) {
+    for (int bi = 0; bi <= WR; ++bi) {
 #pragma unroll
-        for (int bj = 0; bj < BC; ++bj) {
-            const int by = by0 + bi, bx = bx0 + bj;
+        for (int bj = 0; bj <= WC; ++bj) {
+            const int by = py0 + bi, bx = px0 + bj;
             int e0 = 0, e1 = 0;
             if (by <= th && bx <= tw) {
                 e0 = s.bstart[by * nbw + bx];
@@ -870,16 +870,15 @@ __device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc
                     const uint32_t row = s.row[e + u];
                     BufIO<T, 4>::load(gr, e + u < e1 ? (row + ch) * (uint32_t)sizeof(T) : kNoRowBytes, gv[u]);
                 }
-                add_bin_terms<WR, WC, OY, OX>(acc, bi, bj, wv, gv);
+                add_bin_terms<WR, WC>(acc, bi, bj, wv, gv);
             }
         }
     }
 }
 
-// Halo-mode tile kernel. It keeps its own copy of the staging and the walk
-// (the same results as stage_pass and walk_bins; its bin scan goes 512 bins
-// at a time): built from those shared functions it took 1-2% longer (more
-// scalar registers spilled).
+// Halo-mode tile kernel. It keeps its own copy of the staging (the same
+// results as stage_pass; its bin scan goes 512 bins at a time): built from
+// that function it took 1-2% longer (more scalar registers spilled).
 template <typename T, int LPU, int RW>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
@@ -1264,7 +1263,7 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             }
             // bins py0..py0+RH, px0..px0+PC reach the block (bin (by, bx)
             // is anchored at band-local pixel (by - 1, bx - 1))
-            if (own) walk_bins<T, RH + 1, PC + 1, RH, PC, 0, 0>(s, gr, ch, py0, px0, th, tw, nbw, acc);
+            if (own) walk_bins<T, RH, PC>(s, gr, ch, py0, px0, th, tw, nbw, acc);
             if (!single) __syncthreads();  // the next pass is staged over this one
             wr = wn;
         }
