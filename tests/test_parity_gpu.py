@@ -118,6 +118,19 @@ def test_backward_flag_sweep(mode, gpu_device):
     _check_backward(d, gpu_device, f"sweep {mode}")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("mode", SWEEP, ids=lambda m: "-".join(map(str, m)))
+def test_backward_flag_sweep_halo_mode(mode, dtype, gpu_device):
+    """The sweep on a dense shape (8,000 samples per (b, h, level) against 120
+    and 30 pixels: more than one pixel-mode band's worth), so grad_value goes
+    through the halo-mode tile kernel, its bands split into chunks, in every
+    mode; the default small shapes above take pixel mode."""
+    vl, ll, align, pad = mode
+    d = _mk(seed=6, levels=((10, 12), (5, 6)), B=1, N_h=2, N_q=2000, C_h=8, N_p=4, value_dtype=dtype,
+            value_layout=vl, loc_layout=ll, align=align, pad=pad)
+    _check_backward(d, gpu_device, f"sweep halo mode {mode} {dtype}")
+
+
 # ---------------------------------------------------- shapes and edge cases ---
 
 @pytest.mark.parametrize("C_h", [1, 2, 3, 4, 5, 16, 32, 64, 100, 256, 300])
