@@ -310,6 +310,61 @@ def test_pixel_mode_repeat_runs_are_stable(gpu_device):
                                                           compute_grad_attention_weights=False)[0], RTOL["fp32"])
 
 
+def _check_pile_up(d, dev, tag, runs=2):
+    """Oracle parity of all three gradients, grad_value judged against the
+    magnitude of its terms as well (its elements sum thousands of cancelling
+    terms), then grad_value bitwise the same on every further run."""
+    _say(f"backward {tag}")
+    got = _gpu_backward(d, dev)
+    want = oracle_backward(d)
+    mag = oracle_backward(d, grad_output=np.abs(d["grad_output"]),
+                          attention_weights=np.abs(d["attention_weights"]),
+                          compute_grad_sampling_locations=False, compute_grad_attention_weights=False)[0]
+    rtol = RTOL[d["value_dtype"]]
+    compare(f"grad_value {tag}", got[0], want[0], rtol, magnitude=mag)
+    compare(f"grad_sampling_locations {tag}", got[1], want[1], rtol)
+    compare(f"grad_attention_weights {tag}", got[2], want[2], rtol)
+    gv = [_gpu_backward(d, dev, (True, False, False))[0] for _ in range(runs)]
+    for r in [got[0]] + gv:
+        np.testing.assert_array_equal(gv[0], r)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("pad", ["zeros", "border"])
+def test_pile_up_on_one_point(dtype, pad, gpu_device):
+    """All 6,000 samples per (b, h) of the 24x30 level at one location: one
+    anchor bin holds every entry of its band's three LDS passes (2,048 a
+    pass), far past what one lane ranks alone, so whole waves rank them; the
+    6x7 level's samples stay spread."""
+    d = _mk(levels=((24, 30), (6, 7)), B=1, N_h=2, N_q=1500, C_h=32, N_p=4, seed=43, value_dtype=dtype,
+            pad=pad)
+    d["sampling_locations"][:, :, :, 0, :, 0] = np.float32(0.4137)
+    d["sampling_locations"][:, :, :, 0, :, 1] = np.float32(0.6211)
+    _check_pile_up(d, gpu_device, f"pile-up on one point {dtype} {pad}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("align", [False, True])
+def test_border_clamping_piles_up_on_edges(dtype, align, gpu_device):
+    """Border padding with locations in [-1, 2]: two thirds of the samples
+    clamp in x, two thirds in y, so each corner pixel of a level takes one
+    ninth of them (about 670 per (b, h) on the 24x30 level) and the edge
+    pixels tens each. Clamped samples alternate between the two anchors that
+    reach their edge pixel with the same weight; the corner bins still pass
+    the size one lane ranks alone."""
+    d = _mk(levels=((24, 30), (6, 7), (1, 3)), B=1, N_h=2, N_q=1500, C_h=32, N_p=4, seed=47,
+            value_dtype=dtype, pad="border", align=align, loc_range=(-1.0, 2.0))
+    _check_pile_up(d, gpu_device, f"border pile-up {dtype} align={align}")
+
+
+def test_border_clamping_in_pixel_mode(gpu_device):
+    """The same clamping on a level with fewer samples than pixels (pixel
+    mode, one band per level), B2QHLP locations, BNLC value."""
+    d = _mk(levels=((60, 80), (12, 16)), B=2, N_h=2, N_q=300, C_h=32, N_p=4, seed=53, pad="border",
+            loc_range=(-1.0, 2.0), value_layout="BNLC", loc_layout="B2QHLP")
+    _check_pile_up(d, gpu_device, "border pile-up, pixel mode")
+
+
 def test_autograd_function_matches_oracle(gpu_device):
     import torch
     from scale_deformable_attention_forward_amd import ms_deformable_attention
