@@ -20,10 +20,10 @@ namespace msda {
 hipError_t launch_forward(const Geometry& g, int bf16, int vec, int64_t value_bytes, const void* value,
                           const float* loc, const float* attn, void* out, hipStream_t stream);
 hipError_t launch_zero_elems(void* p, int64_t n, int elem, hipStream_t stream);
-hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int bf16, int accumulate,
-                                const void* grad_out, const void* value, const float* loc, const float* attn,
-                                void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
-                                hipStream_t stream);
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int glpu, int gvec, int bf16,
+                                int accumulate, const void* grad_out, const void* value, const float* loc,
+                                const float* attn, void* grad_value, float* grad_loc, float* grad_attn,
+                                void* workspace, hipStream_t stream);
 hipError_t launch_backward_generic(const Geometry& g, int lpu, int bf16, int accumulate, const void* grad_out,
                                    const void* value, const float* loc, const float* attn, void* grad_value,
                                    float* grad_loc, float* grad_attn, void* workspace, hipStream_t stream);
@@ -447,8 +447,8 @@ msda_status backward_call(const msda_problem* problem, const void* grad_output, 
     }
 
     // Fast path: 4 channels per lane (one 16-byte float32 or 8-byte bfloat16
-    // load) and the destination-tiled grad_value pass; otherwise one channel
-    // per lane and atomics.
+    // load; see gvec below for the bfloat16 gather) and the destination-tiled
+    // grad_value pass; otherwise one channel per lane and atomics.
     const int64_t C_h = problem->C_h;
     const size_t row_align = 4 * (size_t)z.elem;
     TilePlan tp = {};
@@ -469,9 +469,14 @@ msda_status backward_call(const msda_problem* problem, const void* grad_output, 
         }
     }
     const int lpu = fast ? fast_lanes(C_h) : 1 << ilog2((int)std::min<int64_t>(64, C_h));
+    // the fast path's gather of grad_A and grad_loc: glpu lanes of gvec
+    // channels per unit; bfloat16 rows of whole 16-byte groups take 8 channels
+    // a lane (one 16-byte load per corner), everything else 4 as the tiles do
+    const int gvec = fast && bf16 && C_h % 8 == 0 && aligned(value, 16) && aligned(grad_output, 16) ? 8 : 4;
+    const int glpu = gvec == 8 ? std::max(1, lpu / 2) : lpu;
     const int64_t units = (int64_t)g.B * g.Nh * g.Nq;
-    const int64_t upb = msda::kBlock / lpu;
-    g.lpu_log2 = ilog2(lpu);
+    const int64_t upb = msda::kBlock / glpu;
+    g.lpu_log2 = ilog2(glpu);
     g.chunks = 1;
     g.units = (int32_t)units;
     g.blocks = (int32_t)((units + upb - 1) / upb);
@@ -486,8 +491,8 @@ msda_status backward_call(const msda_problem* problem, const void* grad_output, 
         return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
     }
     if (fast) {
-        e = msda::launch_backward_fast(g, tp, lpu, bf16, accumulate, grad_output, value, sampling_locations,
-                                       attention_weights, grad_value, grad_sampling_locations,
+        e = msda::launch_backward_fast(g, tp, lpu, glpu, gvec, bf16, accumulate, grad_output, value,
+                                       sampling_locations, attention_weights, grad_value, grad_sampling_locations,
                                        grad_attention_weights, workspace, stream);
     } else {
         e = msda::launch_backward_generic(g, lpu, bf16, accumulate, grad_output, value, sampling_locations,

@@ -315,9 +315,10 @@ __device__ __forceinline__ void store_results(const Geometry& g, const float4* s
 }
 
 // ---------------------------------------------------------------------------
-// Fast path, kernel 1: C_h <= 4 * LPU <= 64, C_h % 4 == 0, channel rows
-// aligned to 4 elements. LPU lanes per unit, 4 channels per lane.
-template <typename T, int LPU, bool BUF>
+// Fast path, kernel 1: C_h <= VEC * LPU <= 64, C_h % VEC == 0, channel rows
+// aligned to VEC elements. LPU lanes per unit, VEC channels per lane (4; 8
+// for bfloat16 rows of whole 16-byte groups: one 16-byte load per corner).
+template <typename T, int LPU, bool BUF, int VEC>
 __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int sc_max, ChunkDiv cdiv,
                                                                int64_t value_bytes,
                                                                const T* __restrict__ grad_out,
@@ -327,7 +328,6 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
                                                                float* __restrict__ grad_loc,
                                                                float* __restrict__ grad_attn, AnchorWs ws)
 {
-    constexpr int VEC = 4;
     constexpr int upb = kBlock / LPU;  // units per workgroup
 
     extern __shared__ float4 smem[];
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void backward_fast_kernel(Geometry g, int s
     const UnitIdx ui = unit_index(g, unit_ok ? u : 0);
     const int c0 = lig * VEC;
     const bool lane_ok = unit_ok && c0 < g.Ch;
-    float G[VEC] = {0.f, 0.f, 0.f, 0.f};
+    float G[VEC] = {};
     if (lane_ok && want_dots)
         VecIO<T, VEC>::load(grad_out + ((ui.b * g.Nq + ui.q) * g.Nh + ui.h) * g.Ch + c0, G);
 
@@ -1526,7 +1526,7 @@ static int samples_per_chunk(int S, int upb)
     return sc;
 }
 
-template <typename T, int LPU>
+template <typename T, int LPU, int VEC>
 static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const void* value, const float* loc,
                                 const float* attn, float* grad_loc, float* grad_attn, AnchorWs ws,
                                 hipStream_t stream)
@@ -1537,11 +1537,11 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
     const int64_t value_bytes = (int64_t)g.B * g.L * g.Nh * g.Ch * (int64_t)sizeof(T);
     const ChunkDiv cdiv = make_chunkdiv(g.S, sc);
     if (buffer_loads_ok(value_bytes))
-        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, true>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, true, VEC>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
                            cdiv, value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc,
                            attn, grad_loc, grad_attn, ws);
     else
-        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, false>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
+        hipLaunchKernelGGL((backward_fast_kernel<T, LPU, false, VEC>), dim3(g.blocks), dim3(kBlock), lds, stream, g, sc,
                            cdiv, value_bytes, static_cast<const T*>(grad_out), static_cast<const T*>(value), loc,
                            attn, grad_loc, grad_attn, ws);
     return hipGetLastError();
@@ -1630,17 +1630,21 @@ size_t fast_workspace_layout(const Geometry& g, const TilePlan& tp, void* base, 
     return at;
 }
 
-template <typename T>
+template <typename T, int VEC>
 static hipError_t launch_fast_typed(const Geometry& g, int lpu, const void* grad_out, const void* value,
                                     const float* loc, const float* attn, float* grad_loc, float* grad_attn,
                                     AnchorWs ws, hipStream_t stream)
 {
     switch (lpu) {
-    case 1: return launch_fast_t<T, 1>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
-    case 2: return launch_fast_t<T, 2>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
-    case 4: return launch_fast_t<T, 4>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
-    case 8: return launch_fast_t<T, 8>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
-    case 16: return launch_fast_t<T, 16>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 1: return launch_fast_t<T, 1, VEC>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 2: return launch_fast_t<T, 2, VEC>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 4: return launch_fast_t<T, 4, VEC>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 8: return launch_fast_t<T, 8, VEC>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    case 16:
+        if constexpr (VEC == 4)
+            return launch_fast_t<T, 16, VEC>(g, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+        else
+            return hipErrorInvalidValue;  // 8 lanes cover the 64 channels at most
     default: return hipErrorInvalidValue;
     }
 }
@@ -1661,17 +1665,23 @@ static hipError_t launch_tiles_typed(const Geometry& g, const TilePlan& tp, int 
 
 // Fast path. Every grad_value element is written by exactly one store (no
 // clearing needed); with `accumulate` the store adds the element's old value.
-hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int bf16, int accumulate,
-                                const void* grad_out, const void* value, const float* loc, const float* attn,
-                                void* grad_value, float* grad_loc, float* grad_attn, void* workspace,
-                                hipStream_t stream)
+hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, int glpu, int gvec, int bf16,
+                                int accumulate, const void* grad_out, const void* value, const float* loc,
+                                const float* attn, void* grad_value, float* grad_loc, float* grad_attn,
+                                void* workspace, hipStream_t stream)
 {
     AnchorWs ws = {nullptr, nullptr};
     BandWs bw = {};
     float* partial = nullptr;
     if (grad_value) fast_workspace_layout(g, tp, workspace, &ws, &bw, &partial);
-    hipError_t e = bf16 ? launch_fast_typed<uint16_t>(g, lpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream)
-                        : launch_fast_typed<float>(g, lpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    // the gather: glpu lanes of gvec channels per unit (g.blocks counts its workgroups)
+    hipError_t e = hipErrorInvalidValue;
+    if (!bf16 && gvec == 4)
+        e = launch_fast_typed<float, 4>(g, glpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    else if (bf16 && gvec == 8)
+        e = launch_fast_typed<uint16_t, 8>(g, glpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
+    else if (bf16 && gvec == 4)
+        e = launch_fast_typed<uint16_t, 4>(g, glpu, grad_out, value, loc, attn, grad_loc, grad_attn, ws, stream);
     if (e != hipSuccess || !grad_value) return e;
     const int slabs = g.B * g.Nh;
     // bucket the samples by band, one run per (band, bucketing workgroup)

@@ -407,10 +407,12 @@ def test_backward_flag_sweep_bf16(mode, gpu_device):
     _check_backward(d, gpu_device, f"bf16 sweep {mode}")
 
 
-@pytest.mark.parametrize("C_h", [4, 6, 8, 32, 64, 100])
+@pytest.mark.parametrize("C_h", [4, 6, 8, 12, 24, 32, 40, 64, 100])
 def test_channel_counts_bf16_backward(C_h, gpu_device):
     """C_h % 4 == 0 and <= 64 take the tiled path, the rest the generic one
-    (float32 accumulator in the workspace, converted once)."""
+    (float32 accumulator in the workspace, converted once); on the tiled
+    path C_h % 8 == 0 gathers 8 channels a lane (24 and 40 leave lanes of a
+    unit idle), the others 4."""
     d = _mk(seed=21, C_h=C_h, N_q=29, N_h=2, value_dtype="bf16")
     _check_backward(d, gpu_device, f"bf16 C_h={C_h}")
 
@@ -501,3 +503,26 @@ def test_unaligned_bf16_backward_takes_generic_path(gpu_device):
     want = oracle_backward(d)
     for n, g, w in zip(("grad_value", "grad_loc", "grad_attn"), res, want):
         compare(f"unaligned bf16 {n}", to_numpy(g), w, RTOL["bf16"])
+
+
+def test_bf16_rows_off_16_bytes_gather_four_channels_a_lane(gpu_device):
+    """value and grad_output views 8 bytes (four bfloat16 elements) into their
+    allocations: the tiled path still applies, but its gather of grad_A and
+    grad_loc takes 4 channels a lane instead of 8."""
+    import torch
+    from scale_deformable_attention_forward_amd import msda_backward
+    d = _mk(seed=59, C_h=32, N_q=200, N_h=4, value_dtype="bf16")
+    t = to_device(d, gpu_device)
+    views = {}
+    for name in ("value", "grad_output"):
+        x = t[name]
+        buf = torch.empty(x.numel() + 4, dtype=x.dtype, device=gpu_device)
+        views[name] = buf[4:].view(x.shape)
+        views[name].copy_(x)
+        assert views[name].data_ptr() % 16 == 8
+    res = msda_backward(views["grad_output"], views["value"], d["spatial_shapes"], d["level_start_index"],
+                        t["sampling_locations"], t["attention_weights"])
+    torch.cuda.synchronize()
+    want = oracle_backward(d)
+    for n, g, w in zip(("grad_value", "grad_loc", "grad_attn"), res, want):
+        compare(f"bf16 rows off 16 bytes {n}", to_numpy(g), w, RTOL["bf16"])
