@@ -430,29 +430,30 @@ struct LevelTiles {
     FastDiv rd, cd;  // by R, by CW
 };
 
-// Tile geometry of level l (static indices only, so the plan stays in kernel-argument memory).
+// Tile geometry of level l, which is the same for the whole workgroup: read
+// through pointers into the kernel arguments, as scalar loads at l's offset.
+// (Indexing the arrays by value, the compiler kept every level's entries in
+// scalar registers and spilled hundreds of them in the tile kernels.)
 __device__ __forceinline__ LevelTiles level_tiles(const Geometry& g, const TilePlan& tp, int l)
 {
-    LevelTiles t = {1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, 0, make_fastdiv(1), make_fastdiv(1)};
-#pragma unroll
-    for (int k = 0; k < kMaxLevels; ++k) {
-        if (k == l) {
-            t.H = g.lv.H[k];
-            t.W = g.lv.W[k];
-            t.start = g.lv.start[k];
-            t.R = tp.rows[k];
-            t.CW = tp.cols[k];
-            t.nbr = tp.row_bands[k];
-            t.nbc = tp.col_bands[k];
-            t.nch = tp.chunks[k];
-            t.band0 = tp.band_begin[k];
-            t.job0 = tp.job_begin[k];
-            t.pjob0 = tp.pjob_begin[k];
-            t.part = tp.part_off[k];
-            t.rd = tp.rows_div[k];
-            t.cd = tp.cols_div[k];
-        }
-    }
+    const Geometry* gp = &g;
+    const TilePlan* pp = &tp;
+    l = __builtin_amdgcn_readfirstlane(l);
+    LevelTiles t;
+    t.H = gp->lv.H[l];
+    t.W = gp->lv.W[l];
+    t.start = gp->lv.start[l];
+    t.R = pp->rows[l];
+    t.CW = pp->cols[l];
+    t.nbr = pp->row_bands[l];
+    t.nbc = pp->col_bands[l];
+    t.nch = pp->chunks[l];
+    t.band0 = pp->band_begin[l];
+    t.job0 = pp->job_begin[l];
+    t.pjob0 = pp->pjob_begin[l];
+    t.part = pp->part_off[l];
+    t.rd = pp->rows_div[l];
+    t.cd = pp->cols_div[l];
     return t;
 }
 
