@@ -343,6 +343,18 @@ def test_pile_up_on_one_point(dtype, pad, gpu_device):
     _check_pile_up(d, gpu_device, f"pile-up on one point {dtype} {pad}")
 
 
+def test_pile_up_beside_spread_samples(gpu_device):
+    """A quarter of the 32x32 level's samples at one location, the rest
+    spread: passes hold one bin of hundreds of entries (ranked by whole
+    waves) among bins of a few (ranked by their own lanes), in the same
+    waves."""
+    d = _mk(levels=((32, 32), (4, 4)), B=1, N_h=2, N_q=2000, C_h=32, N_p=4, seed=61, loc_range=(0.0, 1.0))
+    loc = d["sampling_locations"]
+    loc[:, ::4, :, 0, :, 0] = np.float32(0.2718)
+    loc[:, ::4, :, 0, :, 1] = np.float32(0.5772)
+    _check_pile_up(d, gpu_device, "pile-up beside spread samples")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("align", [False, True])
 def test_border_clamping_piles_up_on_edges(dtype, align, gpu_device):
