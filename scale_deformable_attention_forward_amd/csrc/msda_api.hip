@@ -182,16 +182,13 @@ bool fast_backward_shape(const msda_problem& p)
 // own pixel blocks; so do levels small enough for one such band. Every
 // other level takes halo mode: the
 // (rows + 1) x (cols + 1) anchor bins of a band are dealt out to ny x nx lane
-// groups in blocks of kRectRows x RW bins (ny * nx <= the groups of one tile
-// workgroup), so rows = ny * kRectRows - 1 and cols = nx * RW - 1 (or the
-// level's size), with at most kTileBins anchor bins; of those shapes the one
-// with the fewest tiles is taken (then the fewest column bands: a sample is
-// listed once per band its 2x2 corner block touches). RW is
-// kRectColsSparse when the samples are sparse (fewer samples per slab and
-// level than pixels in the largest level: a tile job's cost is then mostly
-// per job, and wider blocks halve the jobs), else kRectColsDense (a
-// narrower accumulator window is cheaper per entry). The choice depends on
-// the shapes only. At most kMaxBandsPerLevel bands per level. A
+// groups in blocks of kRectRows x kRectCols bins (ny * nx <= the groups of
+// one tile workgroup), so rows = ny * kRectRows - 1 and cols = nx *
+// kRectCols - 1 (or the level's size), with at most kTileBins anchor bins;
+// of those shapes the one with the fewest tiles is taken (then the fewest
+// column bands: a sample is listed once per band its 2x2 corner block
+// touches). The choices depend on the shapes only. At most
+// kMaxBandsPerLevel bands per level. A
 // band whose list is expected to hold more than three LDS passes of entries
 // (coarse levels, where many samples land on each pixel) is split into
 // chunks of its list of about three passes, one workgroup each (smaller
@@ -201,12 +198,7 @@ bool fast_backward_shape(const msda_problem& p)
 // Returns false if a level cannot be tiled that way.
 bool plan_tiles(const msda_problem& p, int lpu, TilePlan* tp)
 {
-    constexpr int64_t RH = msda::kRectRows;
-    int64_t max_pixels = 1;
-    for (int64_t l = 0; l < p.N_l; ++l)
-        max_pixels = std::max<int64_t>(max_pixels, p.spatial_shapes[2 * l] * p.spatial_shapes[2 * l + 1]);
-    const int64_t RW = p.N_q * p.N_p < max_pixels ? msda::kRectColsSparse : msda::kRectColsDense;
-    tp->rect_cols = (int32_t)RW;
+    constexpr int64_t RH = msda::kRectRows, RW = msda::kRectCols;
     const int64_t groups = msda::kTileBlock / lpu;
     const int64_t nsamp = p.N_q * p.N_p;
     const int64_t nwg = std::max<int64_t>(1, (nsamp + msda::kBandChunk - 1) / msda::kBandChunk);

@@ -649,9 +649,9 @@ __device__ __forceinline__ void store_grad4(T* dst, float4 a, int accumulate)
 // (x0..x0+1, y0..y0+1). Two ways of walking the bins, chosen per level:
 //  - halo mode (levels with at least as many samples as pixels): the band's
 //    anchor bins (anchor rows r0-1..r1-1, columns c0-1..c1-1) are dealt out
-//    to the kTileBlock / LPU groups in blocks of kRectRows x RW bins; a
-//    group's block reaches (kRectRows + 1) x (RW + 1) pixels: its own
-//    kRectRows x RW and a halo row above and column to the left, which
+//    to the kTileBlock / LPU groups in blocks of kRectRows x kRectCols bins; a
+//    group's block reaches (kRectRows + 1) x (kRectCols + 1) pixels: its own
+//    kRectRows x kRectCols and a halo row above and column to the left, which
 //    belong to the neighbouring groups. Every entry's grad_output row is
 //    thus loaded once and applied to all four corners; after the passes the
 //    groups hand their halos to their neighbours through LDS, which add
@@ -943,12 +943,12 @@ __device__ __forceinline__ void walk_bins(const TileLds& s, __amdgpu_buffer_rsrc
 // Halo-mode tile kernel. It keeps its own copy of the staging (the same
 // results as stage_pass; its bin scan goes 512 bins at a time): built from
 // that function it took 1-2% longer (more scalar registers spilled).
-template <typename T, int LPU, int RW>
+template <typename T, int LPU>
 __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4))) void tile_scatter_kernel(
     Geometry g, TilePlan tp, BandWs w, const T* __restrict__ grad_out, T* __restrict__ grad_value,
     float* __restrict__ partial, int accumulate)
 {
-    constexpr int RH = kRectRows;
+    constexpr int RH = kRectRows, RW = kRectCols;
     constexpr int E = kTileEntries;
     constexpr int kWaves = kTileBlock / kWave;
     // entries in (bin, k) order: the corner weights A (1-fy)(1-fx), A (1-fy) fx,
@@ -1548,7 +1548,7 @@ static hipError_t launch_fast_t(const Geometry& g, const void* grad_out, const v
     return hipGetLastError();
 }
 
-template <typename T, int LPU, int RW>
+template <typename T, int LPU>
 static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
                                void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
@@ -1557,7 +1557,7 @@ static void launch_tile_kernel(const Geometry& g, const TilePlan& tp, BandWs w, 
     // buffer loads reach every row
     const int64_t blocks = (int64_t)tp.jobs * g.B * g.Nh;
     if (blocks > 0)
-        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU, RW>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
+        hipLaunchKernelGGL((tile_scatter_kernel<T, LPU>), dim3((unsigned)blocks), dim3(kTileBlock), 0, stream,
                            g, tp, w, static_cast<const T*>(grad_out), static_cast<T*>(grad_value), partial,
                            accumulate);
     const int64_t pblocks = (int64_t)tp.pjobs * g.B * g.Nh;
@@ -1570,10 +1570,7 @@ template <typename T, int LPU>
 static hipError_t launch_tiles_t(const Geometry& g, const TilePlan& tp, BandWs w, const void* grad_out,
                                  void* grad_value, float* partial, int accumulate, hipStream_t stream)
 {
-    if (tp.rect_cols == kRectColsSparse)
-        launch_tile_kernel<T, LPU, kRectColsSparse>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
-    else
-        launch_tile_kernel<T, LPU, kRectColsDense>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
+    launch_tile_kernel<T, LPU>(g, tp, w, grad_out, grad_value, partial, accumulate, stream);
     if (tp.rpieces > 0)
         hipLaunchKernelGGL((band_reduce_kernel<T>), dim3((unsigned)tp.rpieces, (unsigned)(g.B * g.Nh)), dim3(kBlock),
                            0, stream, g, tp, partial, static_cast<T*>(grad_value), accumulate);

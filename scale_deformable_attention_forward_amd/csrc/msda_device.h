@@ -83,9 +83,8 @@ struct Geometry {
 // chunks write float32 partial tiles, which a reduction pass adds in chunk
 // order.
 constexpr int kTileBlock = 512;          // threads per tile workgroup
-constexpr int kRectRows = 2;             // a lane group owns kRectRows x (2 or 4) anchor bins:
-constexpr int kRectColsDense = 2;        //   2 columns where samples are dense (cheaper per entry),
-constexpr int kRectColsSparse = 4;       //   4 where they are sparse (twice the band width: half the jobs)
+constexpr int kRectRows = 2;             // halo mode: a lane group owns kRectRows x kRectCols anchor bins
+constexpr int kRectCols = 2;
 constexpr int kTileEntries = 2048;       // list entries staged in LDS per pass
 constexpr int kTileBins = 1536;          // anchor bins per tile: (rows + 1) * (cols + 1)
 constexpr int kPixCols = 4;              // pixel mode: a lane group's block is kRectRows x kPixCols pixels
@@ -117,7 +116,6 @@ struct TilePlan {
     int32_t rpiece_begin[kMaxLevels + 1];
     FastDiv rows_div[kMaxLevels];        // by rows[l]
     FastDiv cols_div[kMaxLevels];        // by cols[l]
-    int32_t rect_cols;                   // anchor-bin columns per lane group (kRectColsDense / kRectColsSparse)
 };
 
 // Workgroups are dealt to the XCDs round-robin (block i runs on XCD i % 8).

@@ -275,12 +275,11 @@ def test_many_runs_in_one_pass(gpu_device):
     _check_backward(d, gpu_device, "many runs in one pass")
 
 
-def test_sparse_samples_wide_blocks_and_split_band(gpu_device):
+def test_sparse_samples_and_split_band(gpu_device):
     """16,000 samples per (b, h, level) against 18,000 pixels in the large
     level: the tile pass walks that level in pixel mode, and the 6x7 level
-    (halo mode with 2x4-bin blocks per lane group: the shape is sparse) has
-    one band holding every sample of that level, so it is split into chunks
-    whose partial tiles the reduction adds."""
+    (halo mode) has one band holding every sample of that level, so it is
+    split into chunks whose partial tiles the reduction adds."""
     d = _mk(levels=((120, 150), (6, 7)), B=1, N_h=2, N_q=4000, C_h=32, N_p=4, seed=31, loc_range=(-0.05, 1.05))
     _check_backward(d, gpu_device, "sparse shape, split band")
 
