@@ -147,12 +147,14 @@ def byte_counts(d):
 
 def measured_traffic():
     """Memory-side bytes per forward launch and per backward call from the
-    committed rocprofv3 counter summary: reads = 32 x TCC_EA0_RDREQ_DRAM_32B
-    (the L2's read requests to memory in 32-byte units, whatever their
-    size), writes = WRITE_SIZE (TCC_EA0_WRREQ in 32- and 64-byte units);
-    both checked there against a plain 1 GiB device copy. Also each kernel's
-    L2 hit rate and atomic request counts. (None, None, {}) when a kernel
-    source changed since the counters were taken."""
+    committed rocprofv3 counter summary: reads = FETCH_SIZE scaled by what it
+    reads on a plain 1 GiB device copy (x 2.0 on this part), writes =
+    WRITE_SIZE (TCC_EA0_WRREQ in 32- and 64-byte units, exact on the copy).
+    The reads agree within 0.4% with 32 x TCC_EA0_RDREQ_DRAM_32B (the L2's
+    read requests to memory in 32-byte units), which is used where FETCH_SIZE
+    was not taken (the generic path) and reported beside it. Also each
+    kernel's L2 hit rate and atomic request counts. (None, None, {}) when a
+    kernel source changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -165,8 +167,10 @@ def measured_traffic():
     per = {}
     for name, c in rec["per_dispatch"].items():
         n = c["dispatches_per_call"]
-        b = (c["read_bytes"] + c["write_bytes"]) * n
-        per[name] = {"hbm_bytes_per_call": b, "read_bytes_per_call": c["read_bytes"] * n,
+        rd = c.get("fetch_bytes_copy_scaled", c["read_bytes"])
+        b = (rd + c["write_bytes"]) * n
+        per[name] = {"hbm_bytes_per_call": b, "read_bytes_per_call": rd * n,
+                     "read_bytes_request_counter_per_call": c["read_bytes"] * n,
                      "write_bytes_per_call": c["write_bytes"] * n, "l2_hit_pct": c.get("L2_hit_pct"),
                      "tcc_atomic_per_call": c.get("TCC_ATOMIC", 0.0) * n}
         if name.startswith("forward_kernel"):
@@ -701,7 +705,8 @@ def main():
         "note": "achieved = counted algorithmic bytes of one launch (corners in range with nonzero weight x "
                 "C_h x 4 B, re-gather and scatter counted once each, plus every stream once) / its mean "
                 "HIP-event time on the launch stream; traffic = memory-side bytes per launch from rocprofv3 "
-                "TCC_EA0_RDREQ_DRAM_32B and WRITE_SIZE (profiles/), null once a kernel source changed",
+                "FETCH_SIZE (x 2.0, what a 1 GiB copy gives; within 0.4% of 32 x TCC_EA0_RDREQ_DRAM_32B) "
+                "and WRITE_SIZE (x 1.0 on the copy) (profiles/), null once a kernel source changed",
     }
     res = {
         "metric": METRIC,
