@@ -1028,9 +1028,9 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
         }
         const int m_cnt = run_off[wn] - p0;
         wr = wn;
-        // stage a pass of list entries and count them per anchor bin
-        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
-        __syncthreads();
+        // stage a pass of list entries and count them per anchor bin; the
+        // entries' loads are issued before the bin counts are cleared, so
+        // their latency covers the clearing and its barrier
         // (each thread keeps its entries' sample indices, bins and records in
         // registers until it writes them to LDS in their sorted place)
         constexpr int kStage = kTileEntries / kTileBlock;
@@ -1051,6 +1051,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             if (tid + u * kTileBlock < m_cnt)
                 rc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(srec + kk[u]));
         }
+        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = 0;
+        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = tid + u * kTileBlock;
