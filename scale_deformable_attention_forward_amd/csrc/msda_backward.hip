@@ -1066,7 +1066,8 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             atomicAdd(&s_cursor[bn[u]], 1);
         }
         __syncthreads();
-        // exclusive scan of the bin counts
+        // exclusive scan of the bin counts into the bin starts and the
+        // placement cursors
         for (int base = 0; base < nbins; base += kTileBlock) {
             const int i = base + tid;
             const int v = i < nbins ? s_cursor[i] : 0;
@@ -1081,7 +1082,10 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             __syncthreads();
             int before = base == 0 ? 0 : s_bstart[base];
             for (int ww = 0; ww < wave; ++ww) before += s_wave[ww];
-            if (i < nbins) s_bstart[i] = before + incl - v;
+            if (i < nbins) {
+                s_bstart[i] = before + incl - v;
+                s_cursor[i] = before + incl - v;  // (only this thread read s_cursor[i])
+            }
             if (tid == kTileBlock - 1) {
                 int tot = base == 0 ? 0 : s_bstart[base];
                 for (int ww = 0; ww < kWaves; ++ww) tot += s_wave[ww];
@@ -1089,8 +1093,6 @@ __global__ __launch_bounds__(kTileBlock) __attribute__((amdgpu_waves_per_eu(4)))
             }
             __syncthreads();
         }
-        for (int i = tid; i < nbins; i += kTileBlock) s_cursor[i] = s_bstart[i];
-        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kStage; ++u)
             if (tid + u * kTileBlock < m_cnt) s_bkey[atomicAdd(&s_cursor[bn[u]], 1)] = kk[u];
