@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense float32 matrix-core peak, TFLOP/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix-core peak, TFLOP/s
 # L2 -> CU read ceiling: 8 XCDs, each with a 16-channel L2 that returns one
 # 128-byte line per channel per clock, at the 2.4 GHz peak engine clock
 # (the same figure as 256 CUs x 64 B per clock of vector-memory return).
@@ -440,8 +441,11 @@ def producer_workspace_bytes(binding, q, w, ss, ls):
 def producer_report(a):
     """One JSON line per input dtype: the producer forward, the fused producer
     + sampler against the two-call chain, and the producer backward, with
-    FLOP/s against the float32 matrix-core peak, and the CPU oracle (float64
-    numpy) on a bounded slice of rows."""
+    FLOP/s against the peak of the matrix cores each one runs on (the
+    forward's projection takes bfloat16 operands as they are; the backward's
+    products involve float32 gradients, so they run in float32), the
+    forward's memory-side bytes against the HBM peak, and the CPU oracle
+    (float64 numpy) on a bounded slice of rows."""
     import torch
     import oracle.producer as oprod
     from scale_deformable_attention_forward_amd import binding
@@ -486,19 +490,31 @@ def producer_report(a):
                                                                workspace=pws, stream=stream),
         }
         ms = {k: time_launches(fn, stream, a.steps, a.warmup) for k, fn in fns.items()}
+        fwd_peak = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        el = 2 if dtype == "bf16" else 4
+        # forward bytes: query features and both weight matrices read, reference
+        # points read, locations and weights written (float32)
+        fwd_bytes = (M * w["D"] * el + 3 * w["N_h"] * S * w["D"] * el + M * len(w["levels"]) * 2 * 4
+                     + M * w["N_h"] * S * 3 * 4)
         line = {"producer": f"encoder shape, D={w['D']}, {dtype} inputs", "B": w["B"], "N_q": w["N_q"],
                 "N_h": w["N_h"], "N_l": len(w["levels"]), "N_p": w["N_p"], "D": w["D"], "C_h": w["C_h"],
-                "flop_forward": gemm_flop, "flop_backward": 2 * gemm_flop,
-                "peak_tflops": MFMA_F32_PEAK_TFLOPS, "peak_note": "float32 matrix cores (bfloat16 inputs are "
-                                                                  "widened exactly and multiplied in float32)"}
-        for k, flop in (("forward", gemm_flop), ("fused_forward", None), ("backward", 2 * gemm_flop),
-                        ("sampler", None)):
+                "flop_forward": gemm_flop, "flop_backward": 2 * gemm_flop, "bytes_forward": fwd_bytes,
+                "peak_tflops_forward": fwd_peak, "peak_tflops_backward": MFMA_F32_PEAK_TFLOPS,
+                "peak_note": ("forward: bfloat16 matrix cores (operands as given, float32 accumulation); "
+                              if dtype == "bf16" else "forward: float32 matrix cores; ")
+                + "backward: float32 matrix cores (the gradients are float32)"}
+        for k, flop, peak in (("forward", gemm_flop, fwd_peak), ("fused_forward", None, None),
+                              ("backward", 2 * gemm_flop, MFMA_F32_PEAK_TFLOPS), ("sampler", None, None)):
             r = stats(ms[k])
             if flop:
                 tf = flop / (r["ms_median"] * 1e-3) / 1e12
-                r.update(tflops=tf, frac_of_peak=tf / MFMA_F32_PEAK_TFLOPS)
+                r.update(tflops=tf, frac_of_peak=tf / peak)
             r["queries_per_s"] = M / (r["ms_median"] * 1e-3)
             line[k] = r
+        f = line["forward"]
+        f["hbm_gbs"] = fwd_bytes / (f["ms_median"] * 1e-3) / 1e9
+        f["hbm_frac"] = f["hbm_gbs"] / HBM_PEAK_GBS
+        f["bound"] = "mfma" if gemm_flop / (fwd_peak * 1e12) > fwd_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
         line["fused_forward"]["two_call_chain_ms"] = line["forward"]["ms_median"] + line["sampler"]["ms_median"]
         if not a.no_cpu_baseline:
             rows = 2048

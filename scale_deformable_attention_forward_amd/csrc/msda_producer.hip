@@ -41,6 +41,7 @@
 namespace msda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPRows = 64;              // query rows per workgroup: 4 waves x 16
 constexpr int kPKc = 32;                // K elements staged per step
@@ -57,6 +58,16 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+// bfloat16 operands, float32 accumulation: lane l supplies row l % 16 of A
+// and column l % 16 of B at k = 8 * (l / 16) .. + 7 (the products are exact
+// in float32); the output layout is mfma_16x16x4's (checked with an
+// in-bounds probe).
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+constexpr int kPHStride = kPKc + 8;  // LDS row stride (bfloat16 elements) of staged bfloat16 tiles
 
 // Per-(row, sample) loops run tpr lanes per row and kBlock / tpr rows per
 // pass; a tile of kPRows rows takes at most this many passes (tpr <= 16, 32,
@@ -146,6 +157,18 @@ struct TileRegs {
             if (r < nrows) *reinterpret_cast<float4*>(dst + r * stride + c) = to_float4(q[i]);
         }
     }
+
+    // bfloat16 operands kept as they are (stride in elements)
+    __device__ __forceinline__ void store_raw(uint16_t* dst, int stride, int nrows) const
+    {
+        static_assert(sizeof(Quad<TQ>) == 8, "raw stores are for bfloat16 tiles");
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = threadIdx.x + i * kBlock;
+            const int r = e / PR, c = (e - r * PR) * 4;
+            if (r < nrows) *reinterpret_cast<uint2*>(dst + r * stride + c) = q[i].v;
+        }
+    }
 };
 
 // Row j of head h's projection matrix: the 2S offset rows, then the S logit rows.
@@ -180,6 +203,30 @@ __device__ __forceinline__ void head_projection(const ProducerGeom& pg, const Pr
     wr.load(wrows, 0, pg.D, pg.vec, wrow);
 #pragma unroll
     for (int t = 0; t < CTM; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(TQ) == 2) {
+        // bfloat16 inputs: staged as they are, one 16x16x32 bfloat16 MFMA per
+        // column tile and step (a lane's 8 A and 8 B elements are one 16-byte
+        // LDS read each)
+        uint16_t* hx = reinterpret_cast<uint16_t*>(s_x);
+        uint16_t* hw = reinterpret_cast<uint16_t*>(s_w);
+        const bf16x8* xa = reinterpret_cast<const bf16x8*>(hx + (16 * wave + (lane & 15)) * kPHStride + 8 * (lane >> 4));
+        const uint16_t* wb = hw + (lane & 15) * kPHStride + 8 * (lane >> 4);
+        for (int k0 = 0; k0 < pg.D; k0 += kPKc) {
+            __syncthreads();  // the previous step's tiles are consumed
+            xr.store_raw(hx, kPHStride, kPRows);
+            wr.store_raw(hw, kPHStride, wrows);
+            __syncthreads();
+            if (k0 + kPKc < pg.D) {
+                xr.load(kPRows, k0 + kPKc, pg.D, pg.vec, xrow);
+                wr.load(wrows, k0 + kPKc, pg.D, pg.vec, wrow);
+            }
+            const bf16x8 av = *xa;
+#pragma unroll
+            for (int t = 0; t < CTM; ++t)
+                acc[t] = mfma_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(wb + t * 16 * kPHStride), acc[t]);
+        }
+        return;
+    }
     const float* xa = s_x + (16 * wave + (lane & 15)) * kPStride + (lane >> 4);
     const float* wb = s_w + (lane & 15) * kPStride + (lane >> 4);
     for (int k0 = 0; k0 < pg.D; k0 += kPKc) {
