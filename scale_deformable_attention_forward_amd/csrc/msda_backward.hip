@@ -613,6 +613,109 @@ __global__ __launch_bounds__(kBandBlock) void band_fill_kernel(Geometry g, TileP
     }
 }
 
+// Bucketing in one kernel when every (slab, level) is a single run (N_q *
+// N_p <= kBandChunk: decoder-sized query sets), in place of the three above.
+// One workgroup per (level, slab): it counts the list entries of the slab's
+// earlier levels (every sample once per band its corners touch) for where
+// its level's lists start, counts its own samples per band, turns the counts
+// into the bands' list offsets (the same exclusive prefix over the slab's
+// bands that band_scan_kernel writes) and fills its lists. Grid (level,
+// slab). Dynamic LDS: 2 * max_bands ints.
+constexpr int kBucketItems = kMaxBandsPerLevel / kBandBlock;  // bands scanned per thread
+__global__ __launch_bounds__(kBandBlock) void band_bucket_kernel(Geometry g, TilePlan tp, BandWs w,
+                                                                 const uint32_t* __restrict__ anchor, int max_bands)
+{
+    extern __shared__ int dyn[];
+    int* cnt = dyn;                 // per band of the level: its entries, then the places handed out
+    int* start = cnt + max_bands;   // where each band's list starts
+    __shared__ int s_wave[kBandBlock / kWave];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int l = blockIdx.x, slab = blockIdx.y;
+    const int nsamp = g.Nq * g.Np;
+    int* off = w.off + (size_t)slab * (tp.bands + 1);  // one run per band
+    uint32_t* list = w.k + (size_t)slab * tp.cap;
+    const LevelTiles t = level_tiles(g, tp, l);
+    const int nb = t.nbr * t.nbc;
+    uint32_t a[kRunPerThread];
+    load_run_anchors(anchor + (size_t)(slab * g.Nl + l) * nsamp, 0, nsamp, a);
+    for (int i = tid; i < nb; i += kBandBlock) cnt[i] = 0;
+    // entries of the earlier levels
+    int earlier = 0;
+    for (int le = 0; le < l; ++le) {
+        const LevelTiles te = level_tiles(g, tp, le);
+        uint32_t ae[kRunPerThread];
+        load_run_anchors(anchor + (size_t)(slab * g.Nl + le) * nsamp, 0, nsamp, ae);
+#pragma unroll
+        for (int i = 0; i < kRunPerThread; ++i) {
+            if (ae[i] == 0xffffffffu) continue;
+            int x0, y0, bands[4];
+            unpack_anchor(ae[i], x0, y0);
+            earlier += sample_bands(te, x0, y0, bands);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRunPerThread; ++i) {
+        if (a[i] == 0xffffffffu) continue;
+        int x0, y0, bands[4];
+        unpack_anchor(a[i], x0, y0);
+        const int n = sample_bands(t, x0, y0, bands);
+        for (int j = 0; j < n; ++j) atomicAdd(&cnt[bands[j]], 1);
+    }
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) earlier += __shfl_xor(earlier, d, kWave);
+    if (lane == 0) s_wave[wave] = earlier;
+    __syncthreads();
+    int carry = 0;
+    for (int ww = 0; ww < kBandBlock / kWave; ++ww) carry += s_wave[ww];
+    __syncthreads();  // s_wave is reused below
+    // exclusive prefix of the level's counts, kBucketItems consecutive bands
+    // per thread; the counters restart at zero for the placement
+    const int i0 = tid * kBucketItems;
+    int v[kBucketItems];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kBucketItems; ++j) {
+        v[j] = i0 + j < nb ? cnt[i0 + j] : 0;
+        sum += v[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += u;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int ww = 0; ww < kBandBlock / kWave; ++ww) {
+        before += ww < wave ? s_wave[ww] : 0;
+        total += s_wave[ww];
+    }
+    int run = carry + before + incl - sum;
+#pragma unroll
+    for (int j = 0; j < kBucketItems; ++j) {
+        if (i0 + j < nb) {
+            start[i0 + j] = run;
+            off[t.band0 + i0 + j] = run;
+            cnt[i0 + j] = 0;
+        }
+        run += v[j];
+    }
+    if (l == g.Nl - 1 && tid == 0) off[tp.bands] = carry + total;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRunPerThread; ++i) {
+        if (a[i] == 0xffffffffu) continue;
+        const uint32_t k = (uint32_t)(tid + i * kBandBlock);
+        int x0, y0, bands[4];
+        unpack_anchor(a[i], x0, y0);
+        const int n = sample_bands(t, x0, y0, bands);
+        for (int j = 0; j < n; ++j) list[start[bands[j]] + atomicAdd(&cnt[bands[j]], 1)] = k;
+    }
+}
+static_assert(kMaxBandsPerLevel % kBandBlock == 0, "whole scan items per thread");
+
 // Band of level-local index `band`: rows [r0, r0 + th), columns [c0, c0 + tw).
 struct BandRect {
     int r0, c0, th, tw;
@@ -1687,13 +1790,19 @@ hipError_t launch_backward_fast(const Geometry& g, const TilePlan& tp, int lpu, 
     if (e != hipSuccess || !grad_value) return e;
     const int slabs = g.B * g.Nh;
     // bucket the samples by band, one run per (band, bucketing workgroup)
-    const dim3 bgrid(tp.nwg, g.Nl, slabs);
-    hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
-    hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
     int max_bands = 1;
     for (int l = 0; l < g.Nl; ++l) max_bands = std::max(max_bands, tp.row_bands[l] * tp.col_bands[l]);
-    hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), (size_t)2 * max_bands * sizeof(int), stream, g, tp,
-                       bw, ws.anchor, max_bands);
+    const size_t band_lds = (size_t)2 * max_bands * sizeof(int);
+    if (tp.nwg == 1) {
+        hipLaunchKernelGGL(band_bucket_kernel, dim3(g.Nl, slabs), dim3(kBandBlock), band_lds, stream, g, tp, bw,
+                           ws.anchor, max_bands);
+    } else {
+        const dim3 bgrid(tp.nwg, g.Nl, slabs);
+        hipLaunchKernelGGL(band_count_kernel, bgrid, dim3(kBandBlock), 0, stream, g, tp, ws.anchor, bw.cnt);
+        hipLaunchKernelGGL(band_scan_kernel, dim3(slabs), dim3(kBlock), 0, stream, tp, bw.cnt, bw.off);
+        hipLaunchKernelGGL(band_fill_kernel, bgrid, dim3(kBandBlock), band_lds, stream, g, tp, bw, ws.anchor,
+                           max_bands);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return bf16 ? launch_tiles_typed<uint16_t>(g, tp, lpu, bw, grad_out, grad_value, partial, accumulate, stream)
